@@ -1,0 +1,89 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check the pins fail.
+
+Each mutant is the oracle's own source with one edit; it is loaded into a
+copy of the oracle module, never into the real one.  A pin set that lets a
+mutant through would be too weak to trust.
+"""
+
+import importlib.util
+import inspect
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.attention as attention
+
+MUTANTS = {
+    "drop_D_term": ("ds = f[\"p\"] * (dp - d_row[:, None])", "ds = f[\"p\"] * dp"),
+    "sign_of_D": ("(dp - d_row[:, None])", "(dp + d_row[:, None])"),
+    "dq_missing_scale": ("\"dq\": spec.sm_scale * (ds @ k[lo:hi])", "\"dq\": (ds @ k[lo:hi])"),
+    "dk_transposed_ds": ("(ds.T @ q[rows])", "(ds @ q[rows])"),
+    "dv_without_dropout": ("f[\"p_drop\"].T @ do[rows]", "f[\"p\"].T @ do[rows]"),
+    "dp_without_dropout": ("dp = dp * f[\"z\"] / (1.0 - spec.dropout_p)", "dp = dp"),
+    "dq_uses_v": ("(ds @ k[lo:hi])", "(ds @ v[lo:hi])"),
+    "lse_without_max": ("lse = m + np.log(ell)", "lse = np.log(ell)"),
+    "causal_off_by_one": ("ok &= j <= i", "ok &= j < i + 2"),
+    "window_wrong_side": ("ok &= j >= i - spec.window_left", "ok &= j >= i - spec.window_left - 1"),
+}
+
+
+def _load_mutant(old, new):
+    src = inspect.getsource(attention)
+    assert old in src, old
+    src = src.replace(old, new)
+    spec = importlib.util.spec_from_loader("oracle._mutant", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__dict__["__package__"] = "oracle"
+    sys.modules["oracle._mutant"] = mod
+    exec(compile(src, "oracle/_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_pass(mod):
+    """A compact run of the pins: torch autograd (with and without dropout)."""
+    torch_dtype = torch.float64
+    rng = np.random.default_rng(7)
+    n, d = 24, 4
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    for kw in ({"causal": True}, {"window_left": 2, "window_right": 3},
+               {"dropout_p": 0.3, "seed": 4}):
+        sp = mod.Spec(sm_scale=0.6, **kw)
+        r = mod.head_backward(q, k, v, do, sp)
+        i = torch.arange(n).view(-1, 1)
+        j = torch.arange(n).view(1, -1)
+        ok = torch.ones(n, n, dtype=torch.bool)
+        if sp.causal:
+            ok &= j <= i
+        if sp.window_left >= 0:
+            ok &= j >= i - sp.window_left
+        if sp.window_right >= 0:
+            ok &= j <= i + sp.window_right
+        tq, tk, tv = (torch.tensor(x, dtype=torch_dtype, requires_grad=True) for x in (q, k, v))
+        s = ((tq @ tk.T) * sp.sm_scale).masked_fill(~ok, float("-inf"))
+        p = torch.softmax(s, -1)
+        if sp.dropout_p > 0:
+            z = torch.tensor(oracle.dropout_keep(sp.seed, sp.offset, 0, 0, np.arange(n),
+                                                 np.arange(n), sp.dropout_p), dtype=torch_dtype)
+            p = p * z / (1 - sp.dropout_p)
+        o = p @ tv
+        o.backward(torch.tensor(do))
+        for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+            if not np.allclose(r[name], t.grad.numpy(), rtol=1e-9, atol=1e-10):
+                return False
+        if not np.allclose(r["o"], o.detach().numpy(), rtol=1e-9, atol=1e-10):
+            return False
+    return True
+
+
+def test_unmutated_oracle_passes_compact_pins():
+    assert _pins_pass(_load_mutant("", ""))
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    assert not _pins_pass(_load_mutant(old, new)), name
