@@ -1,0 +1,222 @@
+"""ctypes binding of libfa.so (include/fa.h), with the same names as the C ABI.
+
+Argument marshalling only: every step of the attention forward/backward runs
+in the library's HIP kernels.  The library is loaded on first use from this
+package directory; if it is missing the call raises (there is no fallback).
+
+Low level: fa_abi_version, fa_status_string, fa_fwd, fa_bwd_preprocess,
+fa_bwd_workspace_bytes, fa_bwd, fa_debug_dropout_mask take FaParams /
+FaTensor structures and raw device pointers, exactly like the C functions.
+High level: forward(...) and backward(...) take torch tensors on the GPU,
+allocate the outputs with torch and enqueue on torch's current stream.
+"""
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+ABI_VERSION = 1
+
+STATUS_NAMES = {
+    0: "FA_SUCCESS",
+    1: "FA_ERR_INVALID_VALUE",
+    2: "FA_ERR_NOT_SUPPORTED",
+    3: "FA_ERR_MISALIGNED",
+    4: "FA_ERR_LAUNCH_FAILED",
+    5: "FA_ERR_HIP",
+}
+
+EXPORTS = ("fa_abi_version", "fa_last_hip_error", "fa_status_string", "fa_fwd", "fa_bwd_preprocess",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_debug_dropout_mask")
+
+
+class FaTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class FaParams(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("seqlen", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+                ("deterministic", ctypes.c_int32), ("dropout_p", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        hip = fa_last_hip_error() if status in (4, 5) else 0
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({fa_status_string(status)})"
+                         + (f", hipError_t {hip}" if hip else ""))
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libfa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m flashattention_backward_pass_fa_amd.build`")
+    # torch ships its own HIP runtime under the same soname.  Loading torch
+    # first makes libfa.so bind to that copy, so one runtime (and one set of
+    # streams and allocations) serves both; loading libfa.so first would pull
+    # in a second runtime whose handles torch's streams are not.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    P, T, vp, fp = ctypes.POINTER(FaParams), FaTensor, ctypes.c_void_p, ctypes.c_void_p
+    lib.fa_abi_version.restype = ctypes.c_int
+    lib.fa_abi_version.argtypes = []
+    lib.fa_last_hip_error.restype = ctypes.c_int
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [P, T, T, T, T, fp, vp]
+    lib.fa_bwd_preprocess.restype = ctypes.c_int
+    lib.fa_bwd_preprocess.argtypes = [P, T, T, fp, fp, vp]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_workspace_bytes.argtypes = [P]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [P, T, T, T, T, fp, fp, T, T, T, fp, vp]
+    lib.fa_debug_dropout_mask.restype = ctypes.c_int
+    lib.fa_debug_dropout_mask.argtypes = [P, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    if lib.fa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libfa.so ABI {lib.fa_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------- the C ABI, 1:1
+
+def fa_abi_version():
+    return load_library().fa_abi_version()
+
+
+def fa_last_hip_error():
+    return load_library().fa_last_hip_error()
+
+
+def fa_status_string(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_fwd(params, q, k, v, o, lse, stream):
+    return load_library().fa_fwd(ctypes.byref(params), q, k, v, o, lse, stream)
+
+
+def fa_bwd_preprocess(params, o, dout, delta, dq_acc, stream):
+    return load_library().fa_bwd_preprocess(ctypes.byref(params), o, dout, delta, dq_acc, stream)
+
+
+def fa_bwd_workspace_bytes(params):
+    return load_library().fa_bwd_workspace_bytes(ctypes.byref(params))
+
+
+def fa_bwd(params, q, k, v, dout, lse, delta, dq, dk, dv, dq_acc, stream):
+    return load_library().fa_bwd(ctypes.byref(params), q, k, v, dout, lse, delta, dq, dk, dv,
+                                 dq_acc, stream)
+
+
+def fa_debug_dropout_mask(params, b, h, mask, stream):
+    return load_library().fa_debug_dropout_mask(ctypes.byref(params), b, h, mask, stream)
+
+
+# ------------------------------------------------------ torch-facing helpers
+
+def make_params(shape, dtype, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0,
+                seed=0, offset=0, deterministic=False):
+    """FaParams for a [B, H, N, d] problem; sm_scale None means 1/sqrt(d)."""
+    bsz, nh, n, d = shape
+    return FaParams(dtype=dtype, batch=bsz, heads=nh, seqlen=n, head_dim=d,
+                    sm_scale=(1.0 / math.sqrt(d)) if sm_scale is None else float(sm_scale),
+                    causal=1 if causal else 0, window_left=int(window[0]),
+                    window_right=int(window[1]), deterministic=1 if deterministic else 0,
+                    dropout_p=float(dropout_p), seed=int(seed), offset=int(offset))
+
+
+def tensor_arg(t):
+    """FaTensor view of a [B, H, N, d] torch tensor (d-stride must be 1)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, H, N, d] tensor with unit stride on d")
+    return FaTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, where):
+    if status != 0:
+        raise FaError(status, where)
+
+
+def forward(q, k, v, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0, seed=0,
+            offset=0, stream=None):
+    """O (dtype of q) and L (fp32 [B, H, N]) of softmax attention on q, k, v."""
+    import torch
+    params = make_params(tuple(q.shape), _dtype_code(q), sm_scale, causal, window, dropout_p,
+                         seed, offset)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
+                  ctypes.c_void_p(lse.data_ptr()), _stream(stream)), "fa_fwd")
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0,
+             seed=0, offset=0, deterministic=False, stream=None, workspace=None, delta=None):
+    """dQ, dK, dV (dtype of q): the pre-pass for D, then the backward kernels.
+
+    workspace: optional fp32 tensor of at least fa_bwd_workspace_bytes bytes
+    (atomic mode); allocated here when None.  delta: optional fp32 [B, H, N]
+    output for D.  Returns (dq, dk, dv, delta).
+    """
+    import torch
+    params = make_params(tuple(q.shape), _dtype_code(q), sm_scale, causal, window, dropout_p,
+                         seed, offset, deterministic)
+    st = _stream(stream)
+    if delta is None:
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws_bytes = fa_bwd_workspace_bytes(params)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else ctypes.c_void_p(0)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(fa_bwd_preprocess(params, tensor_arg(o), tensor_arg(dout),
+                             ctypes.c_void_p(delta.data_ptr()), ws_ptr, st), "fa_bwd_preprocess")
+    _check(fa_bwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(dout),
+                  ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                  tensor_arg(dq), tensor_arg(dk), tensor_arg(dv), ws_ptr, st), "fa_bwd")
+    return dq, dk, dv, delta
+
+
+def debug_dropout_mask(shape, b, h, dropout_p, seed, offset=0, device="cuda", stream=None):
+    """The N x N keep mask (uint8) of head (b, h), computed on the GPU."""
+    import torch
+    params = make_params(shape, FA_DTYPE_F32, None, False, (-1, -1), dropout_p, seed, offset)
+    n = shape[2]
+    mask = torch.empty((n, n), dtype=torch.uint8, device=device)
+    _check(fa_debug_dropout_mask(params, b, h, ctypes.c_void_p(mask.data_ptr()), _stream(stream)),
+           "fa_debug_dropout_mask")
+    return mask

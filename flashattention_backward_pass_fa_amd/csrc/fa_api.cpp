@@ -1,0 +1,254 @@
+// fa_api.cpp - the C ABI of include/fa.h: argument validation, then launches.
+//
+// Every check runs before the first HIP call, so invalid arguments are
+// reported without touching (or needing) a device.  After validation the
+// only HIP calls are a device-count query and the kernel launches, each
+// followed by a check of the launch status (a launch that is silently
+// rejected would otherwise leave the outputs unwritten).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxSeq = 1 << 24;
+
+// Last HIP error seen by a call on this thread (diagnostics only).
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fa_status check_params(const fa_params* p) {
+  if (!p) return FA_ERR_INVALID_VALUE;
+  if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_BF16) return FA_ERR_NOT_SUPPORTED;
+  if (p->batch < 1 || p->heads < 1 || p->seqlen < 1 || p->head_dim < 1) return FA_ERR_INVALID_VALUE;
+  if ((int64_t)p->batch * p->heads > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
+  if (p->seqlen > kMaxSeq) return FA_ERR_NOT_SUPPORTED;
+  if (p->dtype == FA_DTYPE_BF16 && p->head_dim != 64 && p->head_dim != 128) return FA_ERR_NOT_SUPPORTED;
+  if (p->dtype == FA_DTYPE_F32 && p->head_dim > 128) return FA_ERR_NOT_SUPPORTED;
+  if (!std::isfinite(p->sm_scale)) return FA_ERR_INVALID_VALUE;
+  if (p->window_left < -1 || p->window_right < -1) return FA_ERR_INVALID_VALUE;
+  if (!(p->dropout_p >= 0.0 && p->dropout_p < 1.0)) return FA_ERR_INVALID_VALUE;
+  if (p->dropout_p > 0.0) {
+    if (std::ceil(p->dropout_p * 4294967296.0) > 4294967295.0) return FA_ERR_INVALID_VALUE;
+    if (p->batch > 65536 || p->heads > 65536 || p->seqlen > 65536) return FA_ERR_NOT_SUPPORTED;
+  }
+  return FA_SUCCESS;
+}
+
+fa_status check_tensor(const fa_params* p, const fa_tensor& t) {
+  if (!t.ptr) return FA_ERR_INVALID_VALUE;
+  if (t.stride_b < 0 || t.stride_h < 0 || t.stride_n < 0) return FA_ERR_INVALID_VALUE;
+  if (p->dtype == FA_DTYPE_BF16) {
+    if (!aligned(t.ptr, 16)) return FA_ERR_MISALIGNED;
+    if ((t.stride_b % 8) || (t.stride_h % 8) || (t.stride_n % 8)) return FA_ERR_MISALIGNED;
+  } else if (!aligned(t.ptr, 4)) {
+    return FA_ERR_MISALIGNED;
+  }
+  return FA_SUCCESS;
+}
+
+fa_status check_vec(const float* v, uintptr_t align) {
+  if (!v) return FA_ERR_INVALID_VALUE;
+  if (!aligned(v, align)) return FA_ERR_MISALIGNED;
+  return FA_SUCCESS;
+}
+
+#define FA_TRY(expr)                      \
+  do {                                    \
+    const fa_status st_ = (expr);         \
+    if (st_ != FA_SUCCESS) return st_;    \
+  } while (0)
+
+fa::TensorView view(const fa_tensor& t) { return fa::TensorView{t.ptr, t.stride_b, t.stride_h, t.stride_n}; }
+
+fa::MaskArgs mask_args(const fa_params* p) {
+  fa::MaskArgs m{};
+  m.n = p->seqlen;
+  m.causal = p->causal ? 1 : 0;
+  m.wl = p->window_left;
+  m.wr = p->window_right;
+  m.dropout = p->dropout_p > 0.0 ? 1 : 0;
+  m.keep_threshold = (uint32_t)std::ceil(p->dropout_p * 4294967296.0);
+  m.keep_scale = (float)(1.0 / (1.0 - p->dropout_p));
+  m.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
+  m.seed_hi = (uint32_t)(p->seed >> 32);
+  m.off_lo = (uint32_t)(p->offset & 0xFFFFFFFFull);
+  m.off_hi = (uint32_t)(p->offset >> 32);
+  return m;
+}
+
+// A usable device must exist before anything is launched.
+fa_status device_ready() {
+  int n = 0;
+  const hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n < 1) {
+    g_last_hip_error = e != hipSuccess ? (int)e : (int)hipErrorNoDevice;
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return FA_ERR_HIP;
+  }
+  return FA_SUCCESS;
+}
+
+fa_status launched(hipError_t e) {
+  if (e == hipSuccess) return FA_SUCCESS;
+  g_last_hip_error = (int)e;
+  if (e == hipErrorLaunchFailure || e == hipErrorInvalidConfiguration || e == hipErrorInvalidValue ||
+      e == hipErrorLaunchOutOfResources || e == hipErrorInvalidDeviceFunction)
+    return FA_ERR_LAUNCH_FAILED;
+  return FA_ERR_HIP;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_SUCCESS: return "success";
+    case FA_ERR_INVALID_VALUE: return "invalid argument value";
+    case FA_ERR_NOT_SUPPORTED: return "configuration not supported";
+    case FA_ERR_MISALIGNED: return "pointer or stride misaligned";
+    case FA_ERR_LAUNCH_FAILED: return "kernel launch failed";
+    case FA_ERR_HIP: return "HIP runtime error (no usable device?)";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                 void* stream) {
+  FA_TRY(check_params(p));
+  FA_TRY(check_tensor(p, q));
+  FA_TRY(check_tensor(p, k));
+  FA_TRY(check_tensor(p, v));
+  FA_TRY(check_tensor(p, o));
+  FA_TRY(check_vec(lse, 4));
+  if (o.ptr == q.ptr || o.ptr == k.ptr || o.ptr == v.ptr || o.ptr == (void*)lse) return FA_ERR_INVALID_VALUE;
+  FA_TRY(device_ready());
+  fa::FwdArgs a{};
+  a.q = view(q);
+  a.k = view(k);
+  a.v = view(v);
+  a.o = view(o);
+  a.lse = lse;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.d = p->head_dim;
+  a.sm_scale = p->sm_scale;
+  a.scale_log2 = p->sm_scale * kLog2e;
+  a.m = mask_args(p);
+  hipStream_t s = (hipStream_t)stream;
+  return launched(p->dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+size_t fa_bwd_workspace_bytes(const fa_params* p) {
+  if (check_params(p) != FA_SUCCESS) return 0;
+  if (p->deterministic) return 0;
+  return (size_t)4 * (size_t)p->batch * (size_t)p->heads * (size_t)p->seqlen * (size_t)p->head_dim;
+}
+
+fa_status fa_bwd_preprocess(const fa_params* p, fa_tensor o, fa_tensor dout, float* delta, float* dq_acc,
+                            void* stream) {
+  FA_TRY(check_params(p));
+  FA_TRY(check_tensor(p, o));
+  FA_TRY(check_tensor(p, dout));
+  FA_TRY(check_vec(delta, 4));
+  if (dq_acc) FA_TRY(check_vec(dq_acc, 16));
+  if ((void*)delta == o.ptr || (void*)delta == dout.ptr || (dq_acc && (void*)dq_acc == (void*)delta))
+    return FA_ERR_INVALID_VALUE;
+  FA_TRY(device_ready());
+  fa::PrepArgs a{};
+  a.o = view(o);
+  a.dout = view(dout);
+  a.delta = delta;
+  a.dq_acc = dq_acc;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.N = p->seqlen;
+  a.d = p->head_dim;
+  a.bf16 = p->dtype == FA_DTYPE_BF16;
+  a.sm_scale = p->sm_scale;
+  return launched(fa::launch_preprocess(a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor dout, const float* lse,
+                 const float* delta, fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc, void* stream) {
+  FA_TRY(check_params(p));
+  FA_TRY(check_tensor(p, q));
+  FA_TRY(check_tensor(p, k));
+  FA_TRY(check_tensor(p, v));
+  FA_TRY(check_tensor(p, dout));
+  FA_TRY(check_tensor(p, dq));
+  FA_TRY(check_tensor(p, dk));
+  FA_TRY(check_tensor(p, dv));
+  FA_TRY(check_vec(lse, 4));
+  FA_TRY(check_vec(delta, 4));
+  const bool atomic = p->dtype == FA_DTYPE_BF16 && !p->deterministic;
+  if (atomic) FA_TRY(check_vec(dq_acc, 16));
+  const void* ins[] = {q.ptr, k.ptr, v.ptr, dout.ptr, lse, delta};
+  void* outs[] = {dq.ptr, dk.ptr, dv.ptr, atomic ? (void*)dq_acc : nullptr};
+  for (void* o : outs) {
+    if (!o) continue;
+    for (const void* i : ins)
+      if (o == i) return FA_ERR_INVALID_VALUE;
+  }
+  if (dq.ptr == dk.ptr || dq.ptr == dv.ptr || dk.ptr == dv.ptr) return FA_ERR_INVALID_VALUE;
+  if (atomic && ((void*)dq_acc == dq.ptr || (void*)dq_acc == dk.ptr || (void*)dq_acc == dv.ptr))
+    return FA_ERR_INVALID_VALUE;
+  FA_TRY(device_ready());
+  fa::BwdArgs a{};
+  a.q = view(q);
+  a.k = view(k);
+  a.v = view(v);
+  a.dout = view(dout);
+  a.dq = view(dq);
+  a.dk = view(dk);
+  a.dv = view(dv);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq_acc = atomic ? dq_acc : nullptr;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.d = p->head_dim;
+  a.sm_scale = p->sm_scale;
+  a.scale_log2 = p->sm_scale * kLog2e;
+  a.m = mask_args(p);
+  hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == FA_DTYPE_F32) return launched(fa::launch_bwd_f32(a, s));
+  FA_TRY(launched(fa::launch_bwd_bf16(a, !atomic, s)));
+  if (atomic) {
+    fa::PrepArgs c{};
+    c.dq = view(dq);
+    c.dq_acc = dq_acc;
+    c.B = p->batch;
+    c.H = p->heads;
+    c.N = p->seqlen;
+    c.d = p->head_dim;
+    c.bf16 = 1;
+    c.sm_scale = p->sm_scale;
+    FA_TRY(launched(fa::launch_dq_convert(c, s)));
+  }
+  return FA_SUCCESS;
+}
+
+fa_status fa_debug_dropout_mask(const fa_params* p, int32_t b, int32_t h, uint8_t* mask, void* stream) {
+  FA_TRY(check_params(p));
+  if (!mask) return FA_ERR_INVALID_VALUE;
+  if (b < 0 || b >= p->batch || h < 0 || h >= p->heads) return FA_ERR_INVALID_VALUE;
+  if (p->seqlen > 65536 || p->batch > 65536 || p->heads > 65536) return FA_ERR_NOT_SUPPORTED;
+  FA_TRY(device_ready());
+  return launched(fa::launch_dropout_mask(mask_args(p), b, h, mask, (hipStream_t)stream));
+}
+
+}  // extern "C"

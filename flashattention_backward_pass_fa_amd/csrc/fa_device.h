@@ -1,0 +1,128 @@
+// fa_device.h - device-side helpers shared by the gfx950 kernels.
+//
+// MFMA operand layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16  A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + s], s = 0..7
+//                             B (16 x 32): lane l holds B[8 * (l / 32) + s][l % 32]
+//                             C (32 x 32): lane l, register r holds
+//                                          C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+// The accumulator of one product therefore has the *column* index across
+// lanes and the row index inside the lane, which is exactly the A/B operand
+// shape "row across lanes, reduction index inside the lane" of a product
+// that reduces over the first product's rows.  Such register-to-operand
+// reuse sees the reduction index in the permuted order
+//   k-step u, slot s, lane half g  ->  row 16 u + 8 (s / 4) + 4 g + s % 4,
+// and the other operand is then read from LDS in that same order.
+//
+// ds_read_tr16_b64 (gfx950): within each group of 16 lanes, lane i, slot s
+// receives element i % 4 of the 8-byte chunk addressed by lane 4 s + i / 4.
+// If lane j of the group addresses row R + j / 4, column C + 4 (j % 4) of a
+// row-major bf16 tile, lane i receives rows R..R+3 of column C + i: a
+// k-inside-lane operand read straight from a row-major tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+// Strided view of one [B, H, N, d] tensor (element strides; d-stride 1).
+struct TensorView {
+  void* ptr;
+  int64_t sb, sh, sn;
+};
+
+// Mask and dropout flags of one call, in the form the kernels use.
+struct MaskArgs {
+  int n;              // sequence length
+  int causal;         // hide j > i
+  int wl, wr;         // window; -1 = unbounded
+  int dropout;        // 0/1
+  uint32_t keep_threshold;  // keep iff Philox word 0 >= threshold
+  float keep_scale;         // 1 / (1 - p)
+  uint32_t seed_lo, seed_hi, off_lo, off_hi;
+};
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// 8 bytes (4 bf16) transposed out of LDS, see the header comment.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// k-inside-lane operand for one 32x32x16 step from a row-major bf16 tile
+// (row stride ld elements): lane l gets rows row_lo + (0..3) and
+// row_hi + (0..3) of column col0 + l % 32, where row_lo/row_hi already
+// include the lane half's offset.  Every lane passes its own row bases.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ld, int row_lo, int row_hi,
+                                             int col0, int lane) {
+  const int j = lane & 15;
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const bf16x4 lo = lds_read_tr(tile + (row_lo + (j >> 2)) * ld + col);
+  const bf16x4 hi = lds_read_tr(tile + (row_hi + (j >> 2)) * ld + col);
+  return concat(lo, hi);
+}
+
+// valid(i, j): key j visible to query i ("Lecture 7", "Mask behaviour").
+__device__ __forceinline__ bool visible(const MaskArgs& m, int i, int j) {
+  bool ok = (i < m.n) & (j < m.n);
+  if (m.causal) ok &= (j <= i);
+  if (m.wl >= 0) ok &= (j >= i - m.wl);
+  if (m.wr >= 0) ok &= (j <= i + m.wr);
+  return ok;
+}
+
+// Philox4x32-10 (Salmon et al., SC'11): word 0 of the block for counter
+// (off_lo, off_hi, (i << 16) | j, (b << 16) | h) under key (seed_lo, seed_hi).
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(M0, c0), lo0 = M0 * c0;
+    const uint32_t hi1 = __umulhi(M1, c2), lo1 = M1 * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0;
+    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  return c0;
+}
+
+__device__ __forceinline__ bool dropout_keep(const MaskArgs& m, int b, int h, int i, int j) {
+  const uint32_t x = philox_word0(m.off_lo, m.off_hi, ((uint32_t)i << 16) | (uint32_t)j,
+                                  ((uint32_t)b << 16) | (uint32_t)h, m.seed_lo, m.seed_hi);
+  return x >= m.keep_threshold;
+}
+
+template <typename T>
+__device__ __forceinline__ T* at(const TensorView& t, int b, int h, int n) {
+  return (T*)t.ptr + (int64_t)b * t.sb + (int64_t)h * t.sh + (int64_t)n * t.sn;
+}
+
+}  // namespace fa

@@ -1,0 +1,203 @@
+// fa_fwd_bf16.hip - bf16 FlashAttention forward for gfx950, emitting O and L.
+//
+// "FlashAttention backward", section "What the forward left behind": the
+// forward keeps only O and the per-row log-sum-exp L_i = m_i + log l_i.
+// One workgroup owns 128 queries (32 per wave) of one (b, h) and streams
+// 64-key blocks through LDS.  Each wave computes S^T = K Q^T so that its
+// lanes index queries: the running max m and sum l of the online softmax
+// are then per-lane scalars (one exchange with the other lane half per
+// block), and O^T += V^T P~^T keeps the query index across lanes too, so the
+// per-row rescale is a per-lane multiply.  Dropout multiplies the weights
+// that feed O but not the normaliser l.
+
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D>
+struct FCfg {
+  static constexpr int BQ = 128;
+  static constexpr int BK = 64;
+  static constexpr int NT = 256;
+  static constexpr int LD = D + 16;
+  static constexpr int KT = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int CH = D / 8;
+  static constexpr int LOADS = BK * CH / NT;
+};
+
+__device__ __forceinline__ bf16x8 load8(const bf16* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *(bf16x8*)p = v; }
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+  return z;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) fwd_kernel(FwdArgs a) {
+  using C = FCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][C::BK * C::LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int N = a.m.n;
+  const int q0 = blockIdx.y * C::BQ;
+  const int qw = q0 + 32 * w;
+  const int myq = qw + c;
+
+  bf16x8 qreg[C::KT];
+  {
+    const bool ok = myq < N;
+    const bf16* qp = at<bf16>(a.q, b, h, ok ? myq : 0);
+#pragma unroll
+    for (int t = 0; t < C::KT; ++t) qreg[t] = ok ? load8(qp + 16 * t + 8 * g) : zero8();
+  }
+
+  int k_lo = 0, k_hi = N;
+  if (a.m.causal) k_hi = min(k_hi, q0 + C::BQ);
+  if (a.m.wl >= 0) k_lo = max(k_lo, q0 - a.m.wl);
+  if (a.m.wr >= 0) k_hi = min(k_hi, q0 + C::BQ + a.m.wr);
+  const int jt0 = k_lo / C::BK;
+  const int jt1 = k_lo < k_hi ? (k_hi + C::BK - 1) / C::BK : jt0;
+
+  bf16x8 pk[C::LOADS], pv[C::LOADS];
+  auto load_tile = [&](int jt) {
+    const int k0 = jt * C::BK;
+#pragma unroll
+    for (int x = 0; x < C::LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      const int kr = k0 + row;
+      if (kr < N) {
+        pk[x] = load8(at<bf16>(a.k, b, h, kr) + col);
+        pv[x] = load8(at<bf16>(a.v, b, h, kr) + col);
+      } else {
+        pk[x] = zero8();
+        pv[x] = zero8();
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < C::LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      store8(&sK[buf][row * C::LD + col], pk[x]);
+      store8(&sV[buf][row * C::LD + col], pv[x]);
+    }
+  };
+
+  f32x16 oacc[C::DT];
+#pragma unroll
+  for (int n = 0; n < C::DT; ++n) oacc[n] = f32x16{};
+  float m_run = -INFINITY;  // running max of the log2-scaled scores
+  float l_run = 0.f;        // this lane half's share of the normaliser
+
+  if (jt0 < jt1) {
+    load_tile(jt0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int jt = jt0; jt < jt1; ++jt) {
+    const int buf = (jt - jt0) & 1;
+    const bool has_next = jt + 1 < jt1;
+    if (has_next) load_tile(jt + 1);
+    const bf16* Ks = sK[buf];
+    const bf16* Vs = sV[buf];
+    const int k0 = jt * C::BK;
+
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      st[kt] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < C::KT; ++t) {
+        const bf16x8 ak = load8(Ks + (32 * kt + c) * C::LD + 16 * t + 8 * g);
+        st[kt] = mfma32x32x16(ak, qreg[t], st[kt]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+        float s2 = st[kt][r] * a.scale_log2;
+        if (!visible(a.m, myq, key)) s2 = -INFINITY;
+        st[kt][r] = s2;
+        mx = fmaxf(mx, s2);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int n = 0; n < C::DT; ++n) oacc[n] *= alpha;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(st[kt][r] - m_use);
+        l_run += p;
+        float pd = p;
+        if (a.m.dropout) {
+          const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+          pd = dropout_keep(a.m, b, h, myq, key) ? p * a.m.keep_scale : 0.f;
+        }
+        pb[2 * kt + (r >> 3)][r & 7] = (bf16)pd;
+      }
+    }
+    m_run = m_new;
+#pragma unroll
+    for (int n = 0; n < C::DT; ++n) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 av = tr_operand(Vs, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
+        oacc[n] = mfma32x32x16(av, pb[u], oacc[n]);
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (myq < N) {
+    const float inv = 1.0f / l_tot;
+    bf16* op = at<bf16>(a.o, b, h, myq);
+#pragma unroll
+    for (int n = 0; n < C::DT; ++n) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const bf16x4 v4 = {(bf16)(oacc[n][4 * rr] * inv), (bf16)(oacc[n][4 * rr + 1] * inv),
+                           (bf16)(oacc[n][4 * rr + 2] * inv), (bf16)(oacc[n][4 * rr + 3] * inv)};
+        *(bf16x4*)(op + 32 * n + 8 * rr + 4 * g) = v4;
+      }
+    }
+    if (g == 0) a.lse[(int64_t)bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+  const dim3 grid(a.B * a.H, (a.m.n + 127) / 128);
+  if (a.d == 128)
+    hipLaunchKernelGGL(fwd_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(fwd_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,53 @@
+// fa_kernels.h - argument blocks and host-side launchers of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+
+namespace fa {
+
+// Arguments of the forward kernels.
+struct FwdArgs {
+  TensorView q, k, v, o;
+  float* lse;          // [B, H, N] fp32
+  int B, H, d;
+  float sm_scale;
+  float scale_log2;    // sm_scale * log2(e)
+  MaskArgs m;
+};
+
+// Arguments of the backward kernels.
+struct BwdArgs {
+  TensorView q, k, v, dout, dq, dk, dv;
+  const float* lse;    // [B, H, N] fp32, natural log
+  const float* delta;  // [B, H, N] fp32
+  float* dq_acc;       // [B, H, N, d] fp32 (atomic mode)
+  int B, H, d;
+  float sm_scale;
+  float scale_log2;
+  MaskArgs m;
+};
+
+// Arguments of the pre-pass (D) and the dQ conversion.
+struct PrepArgs {
+  TensorView o, dout, dq;
+  float* delta;
+  float* dq_acc;
+  int B, H, N, d;
+  int bf16;            // element type of o/dout/dq
+  float sm_scale;
+};
+
+// Launchers: return hipSuccess or the launch error.  No validation here;
+// the C-ABI layer validates every argument first.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool deterministic, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_preprocess(const PrepArgs& a, hipStream_t s);
+hipError_t launch_dq_convert(const PrepArgs& a, hipStream_t s);
+hipError_t launch_dropout_mask(const MaskArgs& m, int b, int h, uint8_t* out, hipStream_t s);
+
+}  // namespace fa

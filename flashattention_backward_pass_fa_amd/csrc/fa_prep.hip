@@ -1,0 +1,118 @@
+// fa_prep.hip - HBM-bound helper kernels of the backward.
+//
+//  prep_kernel        D_i = sum_k dO_ik O_ik for every row, fp32 accumulate
+//                     ("FlashAttention backward", section "The gradients, and
+//                     the one scalar that makes them local": one cheap pass
+//                     over dO and O before the main loop), fused with zeroing
+//                     the fp32 dQ accumulator of atomic mode.
+//  dq_convert_kernel  dQ = round_bf16(sm_scale * dQ_acc).
+//  mask_kernel        the dropout keep mask of one head (test aid).
+//
+// prep_kernel: 16 lanes per row, each lane loads 16 contiguous bytes of O
+// and dO per step (fully coalesced rows), multiplies in fp32, and the 16
+// partial sums are combined with lane shuffles.  Rows are walked
+// grid-stride so the grid can be sized to the machine.
+
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per row
+
+__global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
+  const int sub = threadIdx.x & 15;
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const int64_t HN = (int64_t)a.H * a.N;
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < rows;
+       row += (int64_t)gridDim.x * kRowsPerBlock) {
+    const int b = (int)(row / HN);
+    const int rem = (int)(row - b * HN);
+    const int h = rem / a.N, n = rem - h * a.N;
+    float acc = 0.f;
+    if (a.bf16) {
+      const bf16* op = at<bf16>(a.o, b, h, n);
+      const bf16* gp = at<bf16>(a.dout, b, h, n);
+      for (int c0 = sub * 8; c0 < a.d; c0 += 128) {
+        const bf16x8 ov = *(const bf16x8*)(op + c0);
+        const bf16x8 gv = *(const bf16x8*)(gp + c0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)ov[e], (float)gv[e], acc);
+      }
+    } else {
+      const float* op = at<float>(a.o, b, h, n);
+      const float* gp = at<float>(a.dout, b, h, n);
+      for (int c = sub; c < a.d; c += 16) acc = fmaf(op[c], gp[c], acc);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (sub == 0) a.delta[row] = acc;
+    if (a.dq_acc) {
+      float* zrow = a.dq_acc + row * a.d;
+      if ((a.d & 3) == 0) {
+        for (int c4 = sub; c4 * 4 < a.d; c4 += 16) ((f32x4*)zrow)[c4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        for (int c = sub; c < a.d; c += 16) zrow[c] = 0.f;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) dq_convert_kernel(PrepArgs a) {
+  // one thread per 8 consecutive elements of a row
+  const int per_row = a.d / 8;
+  const int64_t total = (int64_t)a.B * a.H * a.N * per_row;
+  const int64_t HN = (int64_t)a.H * a.N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / per_row;
+    const int c0 = (int)(t - row * per_row) * 8;
+    const int b = (int)(row / HN);
+    const int rem = (int)(row - b * HN);
+    const int h = rem / a.N, n = rem - h * a.N;
+    const f32x4* src = (const f32x4*)(a.dq_acc + row * a.d + c0);
+    const f32x4 x0 = src[0], x1 = src[1];
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = (bf16)(x0[e] * a.sm_scale);
+      y[4 + e] = (bf16)(x1[e] * a.sm_scale);
+    }
+    *(bf16x8*)(at<bf16>(a.dq, b, h, n) + c0) = y;
+  }
+}
+
+__global__ void __launch_bounds__(256) mask_kernel(MaskArgs m, int b, int h, uint8_t* out) {
+  const int i = blockIdx.x;
+  const int j = blockIdx.y * 256 + threadIdx.x;
+  if (j < m.n) out[(int64_t)i * m.n + j] = dropout_keep(m, b, h, i, j) ? 1 : 0;
+}
+
+int grid_for(int64_t work_items, int per_block) {
+  int64_t blocks = (work_items + per_block - 1) / per_block;
+  const int64_t cap = 256 * 32;  // enough resident blocks to cover 256 CUs many times
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const PrepArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  hipLaunchKernelGGL(prep_kernel, dim3(grid_for(rows, kRowsPerBlock)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_convert(const PrepArgs& a, hipStream_t s) {
+  const int64_t items = (int64_t)a.B * a.H * a.N * (a.d / 8);
+  hipLaunchKernelGGL(dq_convert_kernel, dim3(grid_for(items, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dropout_mask(const MaskArgs& m, int b, int h, uint8_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(mask_kernel, dim3(m.n, (m.n + 255) / 256), dim3(256), 0, s, m, b, h, out);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,164 @@
+/*
+ * fa.h - FlashAttention forward/backward on AMD MI355X (gfx950), C ABI.
+ *
+ * The backward computes dQ, dK, dV of softmax attention from Q, K, V, the
+ * forward output O, the upstream gradient dO and the per-row log-sum-exp L,
+ * with O(N d) extra memory: each S/P tile is recomputed on chip as
+ * P_ij = exp(S_ij - L_i), with the per-row scalar D_i = sum_k dO_ik O_ik, and
+ * dS = P * (dP - D).  The N x N matrices are never written to memory.
+ *
+ *   "Lecture 7 - Backward Pass and Validation": sections "The math"
+ *   (gradients), "The recomputation trick" (recompute P from the saved LSE),
+ *   "Determinism", "Dropout", "Mask behaviour".
+ *   "FlashAttention backward" (GPU kernels lesson 29): sections "What the
+ *   forward left behind" (O and L_i = m_i + log l_i), "The gradients, and the
+ *   one scalar that makes them local" (D), "The loop structure" (KV-outer
+ *   loop; dQ by atomics or by a separate Q-outer kernel).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors Q, K, V, O, dO, dQ, dK, dV are described by fa_tensor: a device
+ *     pointer and element strides for the batch, head and sequence axes; the
+ *     head-dim axis has stride 1.  [B,H,N,d] contiguous and [B,N,H,d] are
+ *     both expressible.  bf16 tensors need a 16-byte aligned pointer and
+ *     strides that are multiples of 8 elements; fp32 tensors need 4-byte
+ *     alignment.
+ *   - L (lse), D (delta) are fp32, [B,H,N] contiguous.  L is the natural log
+ *     of sum_j exp(S_ij) over the visible keys of row i, with
+ *     S = sm_scale * Q K^T.
+ *   - Ownership: the caller allocates every buffer (device memory) and keeps
+ *     it alive until the work on `stream` completes.  The library allocates
+ *     no device memory, keeps no pointer after a call returns and holds no
+ *     mutable global state; calls are re-entrant.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and the call returns after launch.  FA_SUCCESS means
+ *     the arguments were valid and every launch was accepted; faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - Errors: every argument is validated before any HIP call, so a bad
+ *     argument returns FA_ERR_INVALID_VALUE / FA_ERR_NOT_SUPPORTED /
+ *     FA_ERR_MISALIGNED without touching the device.  A failed launch
+ *     returns FA_ERR_LAUNCH_FAILED, any other HIP error FA_ERR_HIP.  The
+ *     library never aborts and never prints.
+ *   - Outputs must not alias inputs or each other.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum fa_status {
+  FA_SUCCESS = 0,
+  FA_ERR_INVALID_VALUE = 1,  /* null pointer, bad size, stride, window, p */
+  FA_ERR_NOT_SUPPORTED = 2,  /* valid but not implemented (dtype, head dim) */
+  FA_ERR_MISALIGNED = 3,     /* pointer or stride alignment */
+  FA_ERR_LAUNCH_FAILED = 4,  /* a kernel launch was rejected */
+  FA_ERR_HIP = 5             /* another HIP runtime error (e.g. no device) */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_DTYPE_F32 = 0,   /* fp32 inputs/outputs, fp32 arithmetic */
+  FA_DTYPE_BF16 = 1   /* bf16 inputs/outputs, bf16 MFMA with fp32 accumulation */
+} fa_dtype;
+
+/* One tensor of logical shape [B, H, N, d]; element (b, h, n, c) lives at
+ * ptr + b*stride_b + h*stride_h + n*stride_n + c (in elements). */
+typedef struct fa_tensor {
+  void* ptr;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_n;
+} fa_tensor;
+
+/* Flags and sizes of one attention call.
+ *   dtype         FA_DTYPE_F32 or FA_DTYPE_BF16
+ *   batch, heads  B, H >= 1
+ *   seqlen        N >= 1 (queries and keys have the same length)
+ *   head_dim      d: bf16 supports 64 and 128; fp32 supports 1..128
+ *   sm_scale      S = sm_scale * Q K^T (the pages use 1/sqrt(d)); any finite
+ *                 value, 0 included
+ *   causal        non-zero: key j is hidden from query i when j > i
+ *   window_left   -1 = unbounded, else keys j >= i - window_left only
+ *   window_right  -1 = unbounded, else keys j <= i + window_right only
+ *                 (with causal and windows >= 0, key i is always visible, so
+ *                 no row is ever empty)
+ *   dropout_p     probability of dropping an attention weight, in [0, 1);
+ *                 kept weights are scaled by 1/(1 - p).  Requires B, H, N
+ *                 <= 65536 when p > 0.
+ *   seed, offset  Philox4x32-10 stream of the dropout mask: key = seed,
+ *                 counter = (offset, (i << 16) | j, (b << 16) | h); weight
+ *                 (b, h, i, j) is kept iff word 0 >= ceil(p * 2^32).
+ *   deterministic non-zero: dQ by a separate Q-outer kernel, bit-identical
+ *                 run to run; zero: dQ by fp32 atomics into a workspace.
+ */
+typedef struct fa_params {
+  int32_t dtype;
+  int32_t batch;
+  int32_t heads;
+  int32_t seqlen;
+  int32_t head_dim;
+  float sm_scale;
+  int32_t causal;
+  int32_t window_left;
+  int32_t window_right;
+  int32_t deterministic;
+  double dropout_p;
+  uint64_t seed;
+  uint64_t offset;
+} fa_params;
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+/* The hipError_t code behind the last FA_ERR_HIP / FA_ERR_LAUNCH_FAILED
+ * returned on the calling thread (0 if none); diagnostics only. */
+int fa_last_hip_error(void);
+
+/* Static, never-NULL description of a status code. */
+const char* fa_status_string(fa_status status);
+
+/* Forward: O = (P * Z / (1 - p)) V with P = softmax of the masked scores, and
+ * L_i = m_i + log l_i ("FlashAttention backward", "What the forward left
+ * behind").  o: output in the input dtype; lse: fp32 [B,H,N] output. */
+fa_status fa_fwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
+                 fa_tensor o, float* lse, void* stream);
+
+/* Backward pre-pass: D_i = sum_k dO_ik * O_ik, one fp32 scalar per row,
+ * accumulated in fp32 ("FlashAttention backward", "The gradients, and the
+ * one scalar that makes them local").  delta: fp32 [B,H,N] output.
+ * dq_acc: NULL, or the fp32 workspace of fa_bwd (fa_bwd_workspace_bytes),
+ * which this call then zeroes; atomic mode requires that. */
+fa_status fa_bwd_preprocess(const fa_params* params, fa_tensor o, fa_tensor dout,
+                            float* delta, float* dq_acc, void* stream);
+
+/* Bytes of fp32 workspace fa_bwd needs: 4*B*H*N*d when deterministic == 0
+ * (the dQ accumulator, [B,H,N,d] contiguous), else 0. */
+size_t fa_bwd_workspace_bytes(const fa_params* params);
+
+/* Backward: dQ, dK, dV in the input dtype ("Lecture 7", "The math";
+ * "FlashAttention backward", "The loop structure").  lse: L from fa_fwd;
+ * delta: D from fa_bwd_preprocess.  dq_acc: required when deterministic == 0
+ * and zeroed by fa_bwd_preprocess beforehand; ignored (may be NULL)
+ * otherwise.  dK and dV never depend on the mode. */
+fa_status fa_bwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
+                 fa_tensor dout, const float* lse, const float* delta,
+                 fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc,
+                 void* stream);
+
+/* Test aid, O(N^2) by design: writes the N x N keep mask Z (1 = kept, 0 =
+ * dropped; row i = query, column j = key) of head (b, h) to device memory
+ * `mask` (uint8, row-major), using the same device function as the kernels.
+ * Masked-out (invisible) pairs are still written with their Philox value. */
+fa_status fa_debug_dropout_mask(const fa_params* params, int32_t b, int32_t h,
+                                uint8_t* mask, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

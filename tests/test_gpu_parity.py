@@ -1,0 +1,114 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small problems are compared element by element in full (they span several
+tiles and a ragged tail); the measured full-size workloads are compared on
+sampled heads, in the launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+
+from tests.gpu_cases import Case, compare, to_host, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_compare(case, deterministic=False, heads=None):
+    print(f"\n[gpu] {case} deterministic={deterministic} heads={heads}", flush=True)
+    host = case.host_inputs()
+    dev = case.device_inputs(host)
+    gpu = case.run_gpu(dev, deterministic=deterministic)
+    ref = case.run_oracle(host, heads=heads)
+    return compare(case, gpu, ref, heads=heads, names=("o", "delta", "dq", "dk", "dv"), host=host)
+
+
+# ------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_tiny_fp32(deterministic):
+    _run_and_compare(Case(1, 1, 128, 64, "f32", seed=1001), deterministic)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_small_causal_bf16(deterministic):
+    _run_and_compare(Case(2, 4, 1024, 64, "bf16", causal=True, seed=1002), deterministic)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_train_causal_bf16_sampled_heads(deterministic):
+    _run_and_compare(Case(4, 16, 4096, 128, "bf16", causal=True, seed=1003), deterministic,
+                     heads=[(0, 0), (3, 15), (2, 9)])
+
+
+def test_window_dropout_bf16_sampled_heads():
+    _run_and_compare(Case(2, 16, 8192, 64, "bf16", window=(1023, 1023), dropout_p=0.1, seed=1004),
+                     heads=[(0, 0), (1, 13)])
+
+
+def test_long_causal_bf16_sampled_head():
+    _run_and_compare(Case(1, 8, 32768, 128, "bf16", causal=True, seed=1005), heads=[(0, 5)])
+
+
+# ------------------------------------------- ragged shapes and every flag
+
+RAGGED = [
+    # (B, H, N, d, causal, window, p)
+    (1, 2, 1, 64, False, (-1, -1), 0.0),
+    (1, 2, 77, 64, True, (-1, -1), 0.0),
+    (2, 1, 130, 128, False, (-1, -1), 0.0),
+    (1, 3, 1000, 64, True, (-1, -1), 0.0),
+    (1, 2, 1000, 128, False, (100, 37), 0.0),
+    (1, 2, 515, 64, True, (200, -1), 0.0),
+    (2, 2, 700, 128, False, (-1, 0), 0.0),
+    (1, 2, 333, 64, False, (-1, -1), 0.25),
+    (1, 2, 600, 128, True, (-1, -1), 0.1),
+    (1, 1, 900, 64, False, (64, 64), 0.3),
+]
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("B,H,N,d,causal,window,p", RAGGED)
+def test_ragged_bf16(B, H, N, d, causal, window, p, deterministic):
+    _run_and_compare(Case(B, H, N, d, "bf16", causal=causal, window=window, dropout_p=p,
+                          seed=7 + N + d), deterministic)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,window,p", [
+    (1, 2, 1, 32, False, (-1, -1), 0.0),
+    (2, 2, 100, 40, True, (-1, -1), 0.0),
+    (1, 1, 257, 128, False, (30, 5), 0.2),
+    (1, 2, 200, 64, True, (50, -1), 0.0),
+])
+def test_ragged_fp32(B, H, N, d, causal, window, p):
+    _run_and_compare(Case(B, H, N, d, "f32", causal=causal, window=window, dropout_p=p, seed=3 + N))
+
+
+def test_non_default_scale_and_strided_layout():
+    """[B, N, H, d] storage (a transposed view) and sm_scale != 1/sqrt(d)."""
+    import torch
+    from flashattention_backward_pass_fa_amd import binding as fa
+    case = Case(2, 3, 300, 64, "bf16", causal=True, seed=99, sm_scale=0.2)
+    print(f"\n[gpu] strided {case}", flush=True)
+    host = case.host_inputs()
+    dev = case.device_inputs(host)
+    # same values, stored as [B, N, H, d] and viewed back as [B, H, N, d]
+    dev = {k: v.transpose(1, 2).contiguous().transpose(1, 2) for k, v in dev.items()}
+    assert dev["q"].stride(2) == 3 * 64
+    gpu = case.run_gpu(dev)
+    ref = case.run_oracle(host)
+    compare(case, gpu, ref, names=("o", "dq", "dk", "dv"))
+
+
+def test_isolated_backward_from_oracle_forward():
+    """Feed the oracle's O (rounded to bf16) and L into the GPU backward."""
+    import torch
+    case = Case(1, 4, 777, 128, "bf16", causal=True, seed=5)
+    print(f"\n[gpu] isolation {case}", flush=True)
+    host = case.host_inputs()
+    dev = case.device_inputs(host)
+    ref = case.run_oracle(host)
+    o = torch.from_numpy(ref["o"].astype(np.float32)).to(torch.bfloat16).cuda()
+    lse = torch.from_numpy(ref["lse"].astype(np.float32)).cuda()
+    gpu = case.run_gpu(dev, o=o, lse=lse)
+    for name in ("dq", "dk", "dv"):
+        assert_close(name, to_host(gpu[name]), ref[name], "bf16")
