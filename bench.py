@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the attention backward on one MI355X.
+
+One step = one pass of the whole backward hot path over the workload:
+fa_bwd_preprocess (D pre-pass, zeroes the dQ accumulator) then fa_bwd (the
+KV-outer MFMA kernel with fp32-atomic dQ, then the dQ conversion; or, in
+deterministic mode, the KV-outer kernel and the Q-outer dQ kernel).  Q, K, V,
+dO and the forward's O and L are resident in HBM before timing starts.
+
+Default workload: causal bf16, B=4, H=16, N=4096, d=128, sm_scale=1/sqrt(d),
+Q, K, V, dO ~ N(0,1) (seeded, synthetic).  The line printed reports credited
+TFLOP/s (10 d FLOPs per visible pair), the roofline of the dominant launch
+(fa_bwd, timed with HIP events on the stream it runs on) against the bf16
+dense MFMA peak, and the CPU oracle timed on one head of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode atomic|deterministic]
+                       [--workload NAME] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_bwd_bf16.hip",
+                  "flashattention_backward_pass_fa_amd/csrc/fa_device.h"]
+TRAFFIC_FILE = "profiles/dkdv_atomic_train_causal_bf16_traffic.md"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per fa_bwd launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, host):
+    """The fp64 oracle on one head of the workload, on this host's cores."""
+    import oracle
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    spec = oracle.Spec(sm_scale=w.sm_scale, causal=w.causal, window_left=w.window_left,
+                       window_right=w.window_right, dropout_p=w.dropout_p, seed=w.drop_seed,
+                       offset=w.drop_offset)
+    # heads in order until about 10 s of CPU work (at least one, at most all)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        oracle.head_backward(host["q"][b, h], host["k"][b, h], host["v"][b, h],
+                             host["do"][b, h], spec, b, h, chunk=512)
+        done += 1
+        if time.perf_counter() - t0 >= 10.0:
+            break
+    secs = time.perf_counter() - t0
+    from flashattention_backward_pass_fa_amd.flops import credited_flops
+    flops_head = credited_flops(1, 1, w.N, w.d, w.causal, w.window_left, w.window_right)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": done * flops_head / secs / 1e12, "unit": "TFLOP/s",
+            "cores": threads or cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (b,h) heads, fp64 numpy backward with S, P, dS "
+                      f"materialised, {secs:.2f} s; BLAS threads {threads}, host affinity {cores}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", choices=["atomic", "deterministic"], default="atomic")
+    ap.add_argument("--workload", default="train_causal_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the backward is "
+              "measured on one GPU's share; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from flashattention_backward_pass_fa_amd import binding as fa
+    from flashattention_backward_pass_fa_amd.flops import (algorithmic_bytes, credited_flops,
+                                                          tile_fraction)
+    from flashattention_backward_pass_fa_amd.inputs import WORKLOADS, make_workload_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench.py measures the bf16 workloads", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    host = make_workload_inputs(w)
+    t = {n: torch.from_numpy(host[n + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+         for n in ("q", "k", "v", "do")}
+    kw = dict(sm_scale=w.sm_scale, causal=w.causal, window=(w.window_left, w.window_right),
+              dropout_p=w.dropout_p, seed=w.drop_seed, offset=w.drop_offset)
+    o, lse = fa.forward(t["q"], t["k"], t["v"], **kw)
+
+    deterministic = args.mode == "deterministic"
+    params = fa.make_params(w.shape, fa.FA_DTYPE_BF16, deterministic=deterministic, **kw)
+    ws_bytes = fa.fa_bwd_workspace_bytes(params)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+    ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws_bytes else 0)
+    delta = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
+    T = fa.tensor_arg
+    args_pre = (params, T(o), T(t["do"]), ctypes.c_void_p(delta.data_ptr()), ws_ptr)
+    args_bwd = (params, T(t["q"]), T(t["k"]), T(t["v"]), T(t["do"]),
+                ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                T(dq), T(dk), T(dv), ws_ptr)
+    stream = torch.cuda.current_stream(dev)
+    st = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        s1 = fa.fa_bwd_preprocess(*args_pre, st)
+        if ev is not None:
+            ev[1].record(stream)
+        s2 = fa.fa_bwd(*args_bwd, st)
+        if ev is not None:
+            ev[2].record(stream)
+        if s1 or s2:
+            raise RuntimeError(f"library status {s1}/{s2}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in events)
+
+    flops = credited_flops(w.B, w.H, w.N, w.d, w.causal, w.window_left, w.window_right)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    achieved = flops / (bwd_avg * 1e-3) / 1e12
+    traffic = measured_traffic() if not deterministic else None
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    pre_bytes = 2 * w.B * w.H * w.N * w.d * 2 + 4 * w.B * w.H * w.N + ws_bytes
+
+    line = {
+        "metric": "attention-backward TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "window": [w.window_left, w.window_right],
+                   "dropout_p": w.dropout_p, "dq_mode": args.mode},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "fa_bwd launch (KV-outer MFMA kernel"
+                               + (" + Q-outer dQ kernel)" if deterministic else " + dQ conversion)")},
+        "kernels_ms": {"fa_bwd_preprocess": round(pre_avg, 4), "fa_bwd": round(bwd_avg, 4)},
+        "preprocess_GBps": round(pre_bytes / (pre_avg * 1e-3) / 1e9, 1),
+        "step_ms_min_median_p90": [round(step_ms[0], 4), round(step_ms[len(step_ms) // 2], 4),
+                                   round(step_ms[int(0.9 * (len(step_ms) - 1))], 4)],
+        "credited_flops": flops,
+        "algorithmic_bytes": algorithmic_bytes(w.B, w.H, w.N, w.d),
+        "tile_fraction_128": round(tile_fraction(w.N, w.causal, w.window_left, w.window_right, 128, 128), 6),
+        "wall_s_timed": round(wall, 3),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, host)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

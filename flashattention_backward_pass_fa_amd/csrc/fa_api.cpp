@@ -73,6 +73,10 @@ fa::MaskArgs mask_args(const fa_params* p) {
   m.causal = p->causal ? 1 : 0;
   m.wl = p->window_left;
   m.wr = p->window_right;
+  // visible iff i - lo_off <= j <= i + hi_off; 2^30 stands for unbounded
+  m.lo_off = p->window_left >= 0 ? p->window_left : (1 << 30);
+  m.hi_off = p->window_right >= 0 ? p->window_right : (1 << 30);
+  if (p->causal && m.hi_off > 0) m.hi_off = 0;
   m.dropout = p->dropout_p > 0.0 ? 1 : 0;
   m.keep_threshold = (uint32_t)std::ceil(p->dropout_p * 4294967296.0);
   m.keep_scale = (float)(1.0 / (1.0 - p->dropout_p));

@@ -85,6 +85,46 @@ __device__ __forceinline__ bool block_dead(const MaskArgs& m, int q0, int nq, in
   return dead;
 }
 
+// Elementwise step of one 32x32 S/dP accumulator pair of the KV-outer kernel:
+// P = exp2(S * c - L2), masked, dropout, dS = P (dP - D).  Writes the bf16
+// A operands of dV (P~) and dK (dS) for the two 16-query k-steps.
+template <bool GENERAL>
+__device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s, const f32x16& dp,
+                                               const float* sLq, const float* sDq, int g, int b,
+                                               int h, int q0, int key, bf16x8& pa0, bf16x8& pa1,
+                                               bf16x8& da0, bf16x8& da1) {
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
+    const f32x4 d4 = *(const f32x4*)(sDq + 8 * rr + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * rr + e;
+      float p = fast_exp2(s[r] * a.scale_log2 - l4[e]);
+      float dpv = dp[r];
+      float pdrop = p;
+      if (GENERAL) {
+        const int qi = q0 + 8 * rr + 4 * g + e;
+        p = visible(a.m, qi, key) ? p : 0.f;
+        pdrop = p;
+        if (a.m.dropout) {
+          const bool keep = dropout_keep(a.m, b, h, qi, key);
+          pdrop = keep ? p * a.m.keep_scale : 0.f;
+          dpv = keep ? dpv * a.m.keep_scale : 0.f;
+        }
+      }
+      const float ds = p * (dpv - d4[e]);
+      if (r < 8) {
+        pa0[r] = (bf16)pdrop;
+        da0[r] = (bf16)ds;
+      } else {
+        pa1[r - 8] = (bf16)pdrop;
+        da1[r - 8] = (bf16)ds;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- KV-outer
 
 template <int D, bool ATOMIC>
@@ -104,6 +144,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   const int N = a.m.n;
   const int kv0 = blockIdx.y * C::BC;
   const int kvw = kv0 + 32 * w;
+  const int key = kvw + c;  // this lane's key (column of S)
 
   // Query rows that can see at least one of the block's keys.
   int q_lo = 0, q_hi = N;
@@ -116,10 +157,9 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   // This wave's 32 keys: B operands of S = Q K^T and dP = dO V^T.
   bf16x8 kreg[C::KT], vreg[C::KT];
   {
-    const int row = kvw + c;
-    const bool ok = row < N;
-    const bf16* kp = at<bf16>(a.k, b, h, ok ? row : 0);
-    const bf16* vp = at<bf16>(a.v, b, h, ok ? row : 0);
+    const bool ok = key < N;
+    const bf16* kp = at<bf16>(a.k, b, h, ok ? key : 0);
+    const bf16* vp = at<bf16>(a.v, b, h, ok ? key : 0);
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) {
       kreg[t] = ok ? load8(kp + 16 * t + 8 * g) : zero8();
@@ -131,8 +171,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
     for (int x = 0; x < C::BC * C::CH / C::NT; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int key = kv0 + row;
-      store8(sK + row * C::LD + col, key < N ? load8(at<bf16>(a.k, b, h, key) + col) : zero8());
+      const int kr = kv0 + row;
+      store8(sK + row * C::LD + col, kr < N ? load8(at<bf16>(a.k, b, h, kr) + col) : zero8());
     }
   }
 
@@ -195,74 +235,67 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
     const bf16* Qs = sQ[buf];
     const bf16* Os = sO[buf];
     const int q0 = it * C::BR;
-    const bool dead = block_dead(a.m, q0, C::BR, kvw, 32);
-    const bool full = block_full(a.m, q0, C::BR, kvw, 32);
 
-    bf16x8 pa[4], da[4];  // A operands (16-query k-steps) of dV and dK
-    if (!dead) {
-      f32x16 s[2], dp[2];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        s[qt] = f32x16{};
-        dp[qt] = f32x16{};
+    for (int qt = 0; qt < 2; ++qt) {
+      const int qs = q0 + 32 * qt;  // first query of this 32-query sub-tile
+      bf16x8 pa0, pa1, da0, da1;
+      if (!block_dead(a.m, qs, 32, kvw, 32)) {
+        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+        bf16x8 aq[C::KT], ao[C::KT];
 #pragma unroll
         for (int t = 0; t < C::KT; ++t) {
-          const bf16x8 aq = load8(Qs + (32 * qt + c) * C::LD + 16 * t + 8 * g);
-          const bf16x8 ao = load8(Os + (32 * qt + c) * C::LD + 16 * t + 8 * g);
-          s[qt] = mfma32x32x16(aq, kreg[t], s[qt]);
-          dp[qt] = mfma32x32x16(ao, vreg[t], dp[qt]);
+          aq[t] = load8(Qs + (32 * qt + c) * C::LD + 16 * t + 8 * g);
+          ao[t] = load8(Os + (32 * qt + c) * C::LD + 16 * t + 8 * g);
         }
-      }
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * qt + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float l2 = sL[buf][ql];
-          const float dd = sD[buf][ql];
-          float p = fast_exp2(s[qt][r] * a.scale_log2 - l2);
-          float dpv = dp[qt][r];
-          if (!full && !visible(a.m, q0 + ql, kvw + c)) p = 0.f;
-          float pdrop = p;
-          if (a.m.dropout) {
-            const bool keep = dropout_keep(a.m, b, h, q0 + ql, kvw + c);
-            pdrop = keep ? p * a.m.keep_scale : 0.f;
-            dpv = keep ? dpv * a.m.keep_scale : 0.f;
-          }
-          const float ds = p * (dpv - dd);
-          pa[2 * qt + (r >> 3)][r & 7] = (bf16)pdrop;
-          da[2 * qt + (r >> 3)][r & 7] = (bf16)ds;
+        for (int t = 0; t < C::KT; ++t) {
+          s = mfma32x32x16(aq[t], kreg[t], s);
+          dp = mfma32x32x16(ao[t], vreg[t], dp);
         }
-      }
-#pragma unroll
-      for (int n = 0; n < C::DT; ++n) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 bo = tr_operand(Os, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
-          const bf16x8 bq = tr_operand(Qs, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
-          dv_acc[n] = mfma32x32x16(pa[u], bo, dv_acc[n]);
-          dk_acc[n] = mfma32x32x16(da[u], bq, dk_acc[n]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) da[u] = zero8();
-    }
+        const float* sLq = &sL[buf][32 * qt];
+        const float* sDq = &sD[buf][32 * qt];
+        if (block_full(a.m, qs, 32, kvw, 32) && !a.m.dropout)
+          kv_elementwise<false>(a, s, dp, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
+        else
+          kv_elementwise<true>(a, s, dp, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
 
-    if (ATOMIC) {
-      // dS^T of this wave's keys into LDS: sT[key][query].
+        // dV += P~^T dO and dK += dS^T Q over these 32 queries
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+        for (int u2 = 0; u2 < 2; ++u2) {
+          const int u = 2 * qt + u2;
+          bf16x8 bo[C::DT], bq[C::DT];
+#pragma unroll
+          for (int n = 0; n < C::DT; ++n) {
+            bo[n] = tr_operand(Os, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
+            bq[n] = tr_operand(Qs, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
+          }
+#pragma unroll
+          for (int n = 0; n < C::DT; ++n) {
+            dv_acc[n] = mfma32x32x16(u2 ? pa1 : pa0, bo[n], dv_acc[n]);
+            dk_acc[n] = mfma32x32x16(u2 ? da1 : da0, bq[n], dk_acc[n]);
+          }
+        }
+      } else {
+        da0 = zero8();
+        da1 = zero8();
+      }
+      if (ATOMIC) {
+        // dS^T of this wave's keys into LDS: sT[key][query]
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const bf16x8 src = da[2 * qt + (rr >> 1)];
+          const bf16x8 src = rr < 2 ? da0 : da1;
           const int s0 = (rr & 1) * 4;
           const bf16x4 v4 = {src[s0], src[s0 + 1], src[s0 + 2], src[s0 + 3]};
           *(bf16x4*)(sT + (32 * w + c) * C::LDS_T + 32 * qt + 8 * rr + 4 * g) = v4;
         }
       }
-      __syncthreads();
-      // dQ partial of the 64 queries over the block's 128 keys.
+    }
+
+    if (ATOMIC) {
+      lds_barrier();
+      // dQ partial of the 64 queries over the block's 128 keys
       constexpr int MT = D == 128 ? 2 : 1;  // 32-query tiles per wave
       const int nt = D == 128 ? w : (w & 1);
       const int mt0 = D == 128 ? 0 : (w >> 1);
@@ -290,7 +323,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
     }
 
     if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    lds_barrier();
   }
 
   // dK = sm_scale * dS^T Q, dV = P~^T dO: one rounding to bf16 at the store.
@@ -298,10 +331,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   for (int n = 0; n < C::DT; ++n) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (key < N) {
-        at<bf16>(a.dk, b, h, key)[32 * n + c] = (bf16)(dk_acc[n][r] * a.sm_scale);
-        at<bf16>(a.dv, b, h, key)[32 * n + c] = (bf16)(dv_acc[n][r]);
+      const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (kr < N) {
+        at<bf16>(a.dk, b, h, kr)[32 * n + c] = (bf16)(dk_acc[n][r] * a.sm_scale);
+        at<bf16>(a.dv, b, h, kr)[32 * n + c] = (bf16)(dv_acc[n][r]);
       }
     }
   }
@@ -390,50 +423,49 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
     if (has_next) load_tile(jt + 1);
     const bf16* Ks = sK[buf];
     const bf16* Vs = sV[buf];
-    const int k0 = jt * C::BK;
-    const bool dead = block_dead(a.m, qw, 32, k0, C::BK);
-    const bool full = block_full(a.m, qw, 32, k0, C::BK);
-    if (!dead) {
-      f32x16 st[2], dpt[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        st[kt] = f32x16{};
-        dpt[kt] = f32x16{};
+    for (int kt = 0; kt < 2; ++kt) {
+      const int ks = jt * C::BK + 32 * kt;  // first key of this 32-key sub-tile
+      if (block_dead(a.m, qw, 32, ks, 32)) continue;
+      bf16x8 ak[C::KT], av[C::KT];
 #pragma unroll
-        for (int t = 0; t < C::KT; ++t) {
-          const bf16x8 ak = load8(Ks + (32 * kt + c) * C::LD + 16 * t + 8 * g);
-          const bf16x8 av = load8(Vs + (32 * kt + c) * C::LD + 16 * t + 8 * g);
-          st[kt] = mfma32x32x16(ak, qreg[t], st[kt]);
-          dpt[kt] = mfma32x32x16(av, oreg[t], dpt[kt]);
-        }
+      for (int t = 0; t < C::KT; ++t) {
+        ak[t] = load8(Ks + (32 * kt + c) * C::LD + 16 * t + 8 * g);
+        av[t] = load8(Vs + (32 * kt + c) * C::LD + 16 * t + 8 * g);
       }
-      bf16x8 da[4];
+      f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int t = 0; t < C::KT; ++t) {
+        st = mfma32x32x16(ak[t], qreg[t], st);
+        dpt = mfma32x32x16(av[t], oreg[t], dpt);
+      }
+      bf16x8 da0, da1;
+      const bool general = !block_full(a.m, qw, 32, ks, 32) || a.m.dropout;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-          float p = fast_exp2(st[kt][r] * a.scale_log2 - l2);
-          float dpv = dpt[kt][r];
-          if (!full && !visible(a.m, myq, key)) p = 0.f;
-          if (a.m.dropout) {
-            const bool keep = dropout_keep(a.m, b, h, myq, key);
-            dpv = keep ? dpv * a.m.keep_scale : 0.f;
-          }
-          da[2 * kt + (r >> 3)][r & 7] = (bf16)(p * (dpv - dd));
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(st[r] * a.scale_log2 - l2);
+        float dpv = dpt[r];
+        if (general) {
+          const int kr = ks + 8 * (r >> 2) + 4 * g + (r & 3);
+          p = visible(a.m, myq, kr) ? p : 0.f;
+          if (a.m.dropout) dpv = dropout_keep(a.m, b, h, myq, kr) ? dpv * a.m.keep_scale : 0.f;
         }
+        const bf16 v = (bf16)(p * (dpv - dd));
+        if (r < 8) da0[r] = v; else da1[r - 8] = v;
       }
 #pragma unroll
-      for (int n = 0; n < C::DT; ++n) {
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = 2 * kt + u2;
+        bf16x8 bk[C::DT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 bk = tr_operand(Ks, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
-          dq_acc[n] = mfma32x32x16(da[u], bk, dq_acc[n]);
-        }
+        for (int n = 0; n < C::DT; ++n)
+          bk[n] = tr_operand(Ks, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
+#pragma unroll
+        for (int n = 0; n < C::DT; ++n) dq_acc[n] = mfma32x32x16(u2 ? da1 : da0, bk[n], dq_acc[n]);
       }
     }
     if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    lds_barrier();
   }
 
 #pragma unroll

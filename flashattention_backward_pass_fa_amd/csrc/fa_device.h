@@ -47,6 +47,7 @@ struct MaskArgs {
   int n;              // sequence length
   int causal;         // hide j > i
   int wl, wr;         // window; -1 = unbounded
+  int lo_off, hi_off; // visible iff i - lo_off <= j <= i + hi_off (folds causal and window)
   int dropout;        // 0/1
   uint32_t keep_threshold;  // keep iff Philox word 0 >= threshold
   float keep_scale;         // 1 / (1 - p)
@@ -84,12 +85,18 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ld, int row_l
 }
 
 // valid(i, j): key j visible to query i ("Lecture 7", "Mask behaviour").
+// Causal and window bounds are folded into two offsets on the host, so the
+// test is branch-free.
 __device__ __forceinline__ bool visible(const MaskArgs& m, int i, int j) {
-  bool ok = (i < m.n) & (j < m.n);
-  if (m.causal) ok &= (j <= i);
-  if (m.wl >= 0) ok &= (j >= i - m.wl);
-  if (m.wr >= 0) ok &= (j <= i + m.wr);
-  return ok;
+  return (i < m.n) & (j < m.n) & (j >= i - m.lo_off) & (j <= i + m.hi_off);
+}
+
+// Barrier that orders LDS accesses only: global stores and atomics in flight
+// are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Philox4x32-10 (Salmon et al., SC'11): word 0 of the block for counter
