@@ -34,7 +34,8 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_bwd_bf16.hip",
                   "flashattention_backward_pass_fa_amd/csrc/fa_device.h"]
-TRAFFIC_FILE = "profiles/dkdv_atomic_train_causal_bf16_traffic.md"
+TRAFFIC_FILE = "profiles/fa_bwd_{mode}_train_causal_bf16_traffic.md"
+COPY_CALIBRATION_BYTES = 256 << 20   # one plain device copy, for HBM counter calibration
 
 
 def kernel_source_hash():
@@ -45,10 +46,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(mode):
     """HBM bytes per fa_bwd launch from the committed counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(mode=mode))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -96,7 +97,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", choices=["atomic", "deterministic"], default="atomic")
+    ap.add_argument("--mode", choices=["atomic", "deterministic"], default="deterministic")
     ap.add_argument("--workload", default="train_causal_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -125,59 +126,69 @@ def main():
               dropout_p=w.dropout_p, seed=w.drop_seed, offset=w.drop_offset)
     o, lse = fa.forward(t["q"], t["k"], t["v"], **kw)
 
-    deterministic = args.mode == "deterministic"
-    params = fa.make_params(w.shape, fa.FA_DTYPE_BF16, deterministic=deterministic, **kw)
-    ws_bytes = fa.fa_bwd_workspace_bytes(params)
-    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
-    ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws_bytes else 0)
-    delta = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
-    dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
-    T = fa.tensor_arg
-    args_pre = (params, T(o), T(t["do"]), ctypes.c_void_p(delta.data_ptr()), ws_ptr)
-    args_bwd = (params, T(t["q"]), T(t["k"]), T(t["v"]), T(t["do"]),
-                ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
-                T(dq), T(dk), T(dv), ws_ptr)
-    stream = torch.cuda.current_stream(dev)
-    st = ctypes.c_void_p(stream.cuda_stream)
+    def measure(mode):
+        """Time `args.steps` steps of the backward in dQ mode `mode`."""
+        deterministic = mode == "deterministic"
+        params = fa.make_params(w.shape, fa.FA_DTYPE_BF16, deterministic=deterministic, **kw)
+        ws_bytes = fa.fa_bwd_workspace_bytes(params)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+        ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws_bytes else 0)
+        delta = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+        dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
+        T = fa.tensor_arg
+        args_pre = (params, T(o), T(t["do"]), ctypes.c_void_p(delta.data_ptr()), ws_ptr)
+        args_bwd = (params, T(t["q"]), T(t["k"]), T(t["v"]), T(t["do"]),
+                    ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                    T(dq), T(dk), T(dv), ws_ptr)
+        stream = torch.cuda.current_stream(dev)
+        st = ctypes.c_void_p(stream.cuda_stream)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        s1 = fa.fa_bwd_preprocess(*args_pre, st)
-        if ev is not None:
-            ev[1].record(stream)
-        s2 = fa.fa_bwd(*args_bwd, st)
-        if ev is not None:
-            ev[2].record(stream)
-        if s1 or s2:
-            raise RuntimeError(f"library status {s1}/{s2}")
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            s1 = fa.fa_bwd_preprocess(*args_pre, st)
+            if ev is not None:
+                ev[1].record(stream)
+            s2 = fa.fa_bwd(*args_bwd, st)
+            if ev is not None:
+                ev[2].record(stream)
+            if s1 or s2:
+                raise RuntimeError(f"library status {s1}/{s2}")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(events[i])
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(args.steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            step(events[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        return {"ms_per_step": start.elapsed_time(end) / args.steps,
+                "pre_ms": [e[0].elapsed_time(e[1]) for e in events],
+                "bwd_ms": [e[1].elapsed_time(e[2]) for e in events],
+                "step_ms": sorted(e[0].elapsed_time(e[2]) for e in events),
+                "wall": wall, "ws_bytes": ws_bytes, "deterministic": deterministic}
 
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
-    step_ms = sorted(e[0].elapsed_time(e[2]) for e in events)
+    main_run = measure(args.mode)
+    other_mode = "atomic" if args.mode == "deterministic" else "deterministic"
+    other_run = measure(other_mode)
+    deterministic = main_run["deterministic"]
+    ms_per_step = main_run["ms_per_step"]
+    pre_ms, bwd_ms, step_ms = main_run["pre_ms"], main_run["bwd_ms"], main_run["step_ms"]
+    ws_bytes, wall = main_run["ws_bytes"], main_run["wall"]
 
     flops = credited_flops(w.B, w.H, w.N, w.d, w.causal, w.window_left, w.window_right)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     achieved = flops / (bwd_avg * 1e-3) / 1e12
-    traffic = measured_traffic() if not deterministic else None
+    traffic = measured_traffic(args.mode)
     pre_avg = sum(pre_ms) / len(pre_ms)
     pre_bytes = 2 * w.B * w.H * w.N * w.d * 2 + 4 * w.B * w.H * w.N + ws_bytes
 
@@ -211,8 +222,18 @@ def main():
         "algorithmic_bytes": algorithmic_bytes(w.B, w.H, w.N, w.d),
         "tile_fraction_128": round(tile_fraction(w.N, w.causal, w.window_left, w.window_right, 128, 128), 6),
         "wall_s_timed": round(wall, 3),
+        "other_mode": {"dq_mode": other_mode,
+                       "ms_per_step": round(other_run["ms_per_step"], 4),
+                       "value": round(flops / (other_run["ms_per_step"] * 1e-3) / 1e12, 2)},
         "device": torch.cuda.get_device_name(dev),
     }
+    # A plain copy of known size (outside the timed region): profiling runs
+    # use its FETCH_SIZE / WRITE_SIZE to calibrate the HBM byte counters.
+    src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, host)
     print(json.dumps(line), flush=True)

@@ -37,20 +37,28 @@ struct KvCfg {
   static constexpr int BC = 128;          // keys per workgroup
   static constexpr int BR = 64;           // queries per inner iteration
   static constexpr int NT = 256;          // threads (4 waves)
-  static constexpr int LD = D + 16;       // LDS row stride of Q/dO/K tiles
-  static constexpr int LDS_T = BR + 16;   // LDS row stride of the dS^T tile
+  static constexpr int LD = lds_stride(D);  // LDS row stride of Q/dO/K tiles
+  static constexpr int LDS_T = BR + 8;     // LDS row stride of the dS^T tile (36 dwords)
   static constexpr int KT = D / 16;       // MFMA k-steps over d
   static constexpr int DT = D / 32;       // 32-wide tiles over d
   static constexpr int CH = D / 8;        // 16-byte chunks per row
   static constexpr int LOADS = BR * CH / NT;
 };
 
+// Workgroups per CU each kernel is compiled for (2 = two waves per SIMD):
+// register budgets of 256 per lane where the kernel fits in them.
+#ifndef KV_MINB_128
+#define KV_MINB_128 1
+#endif
+template <int D, bool ATOMIC>
+constexpr int kv_min_blocks() { return (D == 64 && !ATOMIC) ? 2 : (D == 128 && !ATOMIC ? KV_MINB_128 : 1); }
+
 template <int D>
 struct QCfg {
   static constexpr int BQ = 128;          // queries per workgroup
   static constexpr int BK = 64;           // keys per inner iteration
   static constexpr int NT = 256;
-  static constexpr int LD = D + 16;
+  static constexpr int LD = lds_stride(D);
   static constexpr int KT = D / 16;
   static constexpr int DT = D / 32;
   static constexpr int CH = D / 8;
@@ -128,7 +136,7 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
 // ---------------------------------------------------------------- KV-outer
 
 template <int D, bool ATOMIC>
-__global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, (kv_min_blocks<D, ATOMIC>())) dkdv_kernel(BwdArgs a) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2][C::BR * C::LD];
   __shared__ __attribute__((aligned(16))) bf16 sO[2][C::BR * C::LD];
@@ -312,6 +320,9 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
           dq[mi] = mfma32x32x16(as, bk, dq[mi]);
         }
       }
+      // The next tile's loads are consumed before this step's atomics are
+      // issued, so waiting for them never waits for the atomics' round trip.
+      if (has_next) store_tile(buf ^ 1);
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
@@ -320,9 +331,9 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
           if (qr < N) unsafeAtomicAdd(a.dq_acc + (row_base + qr) * D + 32 * nt + c, dq[mi][r]);
         }
       }
+    } else if (has_next) {
+      store_tile(buf ^ 1);
     }
-
-    if (has_next) store_tile(buf ^ 1);
     lds_barrier();
   }
 
@@ -343,7 +354,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- Q-outer
 
 template <int D>
-__global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][C::BK * C::LD];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][C::BK * C::LD];

@@ -84,6 +84,15 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ld, int row_l
   return concat(lo, hi);
 }
 
+// Row stride (bf16 elements) of a row-major LDS tile of `cols` columns.
+// Measured on gfx950 (64 banks of 4 bytes): a b128 row read by 16 lanes of
+// consecutive rows is conflict-free when the stride in dwords is an odd
+// multiple of 4 modulo 64, and the transposed 8-byte read, which touches 4
+// consecutive rows x 8 dwords per 16 lanes, needs those 4 row segments on
+// disjoint banks.  76 dwords (128 columns) and 52 dwords (64 columns)
+// satisfy both.
+__host__ __device__ constexpr int lds_stride(int cols) { return cols == 128 ? 152 : 104; }
+
 // valid(i, j): key j visible to query i ("Lecture 7", "Mask behaviour").
 // Causal and window bounds are folded into two offsets on the host, so the
 // test is branch-free.
@@ -131,5 +140,31 @@ template <typename T>
 __device__ __forceinline__ T* at(const TensorView& t, int b, int h, int n) {
   return (T*)t.ptr + (int64_t)b * t.sb + (int64_t)h * t.sh + (int64_t)n * t.sn;
 }
+
+// This wave's share (of 4 waves) of a direct global->LDS load of rows
+// [row0, row0 + ROWS) of tensor t (D columns) into a padded row-major tile
+// of row stride lds_stride(D).  Each wave-wide 16-byte load fills 1 KB of
+// the tile: lane L supplies the global chunk that belongs at tile byte
+// 1024 kb + 16 L.  Pad slots re-read chunk 0 of their row and rows past the
+// sequence end re-read row n - 1, so the tile only holds finite values.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_tile(bf16* tile, const TensorView& t, int b, int h, int row0,
+                                         int n, int w, int lane) {
+  constexpr int CPR = lds_stride(D) / 8;  // 16-byte chunks per padded row
+  constexpr int KB = ROWS * CPR / 64;     // wave-wide loads per tile
+  static_assert(ROWS * CPR % 64 == 0, "tile must be a whole number of KB");
+  for (int kb = w; kb < KB; kb += 4) {
+    const int idx = kb * 64 + lane;
+    const int row = idx / CPR, chunk = idx - row * CPR;
+    const int src = min(row0 + row, n - 1);
+    const bf16* gp = at<bf16>(t, b, h, src) + 8 * (chunk < D / 8 ? chunk : 0);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gp,
+                                     (void FA_LDS*)(tile + kb * 512), 16, 0, 0);
+  }
+}
+
+// Wait until every global load this wave issued (including direct-to-LDS
+// loads) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace fa

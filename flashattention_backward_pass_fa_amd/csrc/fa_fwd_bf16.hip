@@ -22,7 +22,7 @@ struct FCfg {
   static constexpr int BQ = 128;
   static constexpr int BK = 64;
   static constexpr int NT = 256;
-  static constexpr int LD = D + 16;
+  static constexpr int LD = lds_stride(D);
   static constexpr int KT = D / 16;
   static constexpr int DT = D / 32;
   static constexpr int CH = D / 8;
