@@ -351,6 +351,183 @@ __global__ void __launch_bounds__(256, (kv_min_blocks<D, ATOMIC>())) dkdv_kernel
   }
 }
 
+// ------------------------------------------- KV-outer, queries split by wave
+
+// KV-outer kernel with 8 independent waves (two per SIMD).  The workgroup's
+// 128 keys are 4 groups of 32; wave w takes key group w % 4 and query half
+// w / 4 of every 64-query block, and accumulates its own partial dK, dV.
+// K and V of the block sit in LDS (B operands of S and dP read with b128),
+// so a wave holds only its 32 x d dK and dV accumulators: it fits in 256
+// registers.  The two partials of a key group are summed through LDS once,
+// after the loop.
+template <int D>
+struct KvQCfg {
+  static constexpr int BC = 128, BR = 64, NT = 512;
+  static constexpr int LD = lds_stride(D);
+  static constexpr int KT = D / 16, DT = D / 32, CH = D / 8;
+  static constexpr int LOADS = BR * CH / NT;        // Q (and dO) chunks per thread per block
+  static constexpr int KV_LOADS = BC * CH / NT;     // K (and V) chunks per thread, once
+};
+
+template <int D>
+__global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
+  using C = KvQCfg<D>;
+  // [0, 4*BR*LD): Q, dO double buffers; then K and V; reused for the
+  // partial-sum exchange after the loop.
+  constexpr int TILE = C::BR * C::LD, KVT = C::BC * C::LD;
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE + 2 * KVT];
+  __shared__ __attribute__((aligned(16))) float sL[2][C::BR];
+  __shared__ __attribute__((aligned(16))) float sD[2][C::BR];
+  // Q buffers at smem + buf * TILE, dO buffers at smem + (2 + buf) * TILE
+  bf16* sK = smem + 4 * TILE;
+  bf16* sV = sK + KVT;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int grp = w & 3, qh = w >> 2;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int N = a.m.n;
+  const int kv0 = blockIdx.y * C::BC;
+  const int kvw = kv0 + 32 * grp;
+  const int key = kvw + c;
+
+  int q_lo = 0, q_hi = N;
+  if (a.m.causal) q_lo = max(q_lo, kv0);
+  if (a.m.wr >= 0) q_lo = max(q_lo, kv0 - a.m.wr);
+  if (a.m.wl >= 0) q_hi = min(q_hi, kv0 + C::BC + a.m.wl);
+  const int it0 = q_lo / C::BR;
+  const int it1 = q_lo < q_hi ? (q_hi + C::BR - 1) / C::BR : it0;
+
+  // K and V rows of the block into LDS (zeros past the sequence end)
+#pragma unroll
+  for (int x = 0; x < C::KV_LOADS; ++x) {
+    const int chunk = tid + x * C::NT;
+    const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+    const int kr = kv0 + row;
+    store8(sK + row * C::LD + col, kr < N ? load8(at<bf16>(a.k, b, h, kr) + col) : zero8());
+    store8(sV + row * C::LD + col, kr < N ? load8(at<bf16>(a.v, b, h, kr) + col) : zero8());
+  }
+
+  const int64_t row_base = (int64_t)bh * N;
+  bf16x8 pq[C::LOADS], po[C::LOADS];
+  float pld = 0.f;
+  auto load_tile = [&](int it) {
+    const int q0 = it * C::BR;
+#pragma unroll
+    for (int x = 0; x < C::LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      const int qr = min(q0 + row, N - 1);
+      pq[x] = load8(at<bf16>(a.q, b, h, qr) + col);
+      po[x] = load8(at<bf16>(a.dout, b, h, qr) + col);
+    }
+    if (tid < 2 * C::BR) {
+      const int qr = q0 + (tid & (C::BR - 1));
+      pld = qr < N ? (tid < C::BR ? a.lse[row_base + qr] * kLog2e : a.delta[row_base + qr]) : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < C::LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      store8(smem + buf * TILE + row * C::LD + col, pq[x]);
+      store8(smem + (2 + buf) * TILE + row * C::LD + col, po[x]);
+    }
+    if (tid < C::BR) sL[buf][tid] = pld;
+    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = pld;
+  };
+
+  f32x16 dk_acc[C::DT], dv_acc[C::DT];
+#pragma unroll
+  for (int n = 0; n < C::DT; ++n) {
+    dk_acc[n] = f32x16{};
+    dv_acc[n] = f32x16{};
+  }
+
+  if (it0 < it1) {
+    load_tile(it0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const bf16* Kr = sK + (32 * grp + c) * C::LD + 8 * g;  // this lane's key row (B operands)
+  const bf16* Vr = sV + (32 * grp + c) * C::LD + 8 * g;
+  for (int it = it0; it < it1; ++it) {
+    const int buf = (it - it0) & 1;
+    const bool has_next = it + 1 < it1;
+    if (has_next) load_tile(it + 1);
+    const bf16* Qs = smem + buf * TILE;
+    const bf16* Os = smem + (2 + buf) * TILE;
+    const int qs = it * C::BR + 32 * qh;
+    if (!block_dead(a.m, qs, 32, kvw, 32)) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < C::KT; ++t) {
+        const bf16x8 aq = load8(Qs + (32 * qh + c) * C::LD + 16 * t + 8 * g);
+        const bf16x8 ao = load8(Os + (32 * qh + c) * C::LD + 16 * t + 8 * g);
+        sacc = mfma32x32x16(aq, load8(Kr + 16 * t), sacc);
+        dpacc = mfma32x32x16(ao, load8(Vr + 16 * t), dpacc);
+      }
+      bf16x8 pa0, pa1, da0, da1;
+      const float* sLq = &sL[buf][32 * qh];
+      const float* sDq = &sD[buf][32 * qh];
+      if (block_full(a.m, qs, 32, kvw, 32) && !a.m.dropout)
+        kv_elementwise<false>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
+      else
+        kv_elementwise<true>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = 2 * qh + u2;
+        bf16x8 bo[C::DT], bq[C::DT];
+#pragma unroll
+        for (int n = 0; n < C::DT; ++n) {
+          bo[n] = tr_operand(Os, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
+          bq[n] = tr_operand(Qs, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
+        }
+#pragma unroll
+        for (int n = 0; n < C::DT; ++n) {
+          dv_acc[n] = mfma32x32x16(u2 ? pa1 : pa0, bo[n], dv_acc[n]);
+          dk_acc[n] = mfma32x32x16(u2 ? da1 : da0, bq[n], dk_acc[n]);
+        }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    lds_barrier();
+  }
+
+  // Sum the two query halves of each key group: waves 4..7 hand their
+  // partials to waves 0..3 through LDS (value r of tile n of lane l at
+  // ((grp * 2 DT + n) * 16 + r) * 64 + l, one contiguous KB per register).
+  float* xch = (float*)smem;
+  if (qh == 1) {
+#pragma unroll
+    for (int n = 0; n < C::DT; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        xch[((grp * 2 * C::DT + n) * 16 + r) * 64 + lane] = dk_acc[n][r];
+        xch[((grp * 2 * C::DT + C::DT + n) * 16 + r) * 64 + lane] = dv_acc[n][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int n = 0; n < C::DT; ++n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dkv = dk_acc[n][r] + xch[((grp * 2 * C::DT + n) * 16 + r) * 64 + lane];
+        const float dvv = dv_acc[n][r] + xch[((grp * 2 * C::DT + C::DT + n) * 16 + r) * 64 + lane];
+        const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (kr < N) {
+          at<bf16>(a.dk, b, h, kr)[32 * n + c] = (bf16)(dkv * a.sm_scale);
+          at<bf16>(a.dv, b, h, kr)[32 * n + c] = (bf16)(dvv);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- Q-outer
 
 template <int D>
@@ -494,7 +671,10 @@ hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
   const int bh = a.B * a.H;
   const dim3 grid_kv(bh, (a.m.n + KvCfg<D>::BC - 1) / KvCfg<D>::BC);
   if (deterministic) {
-    hipLaunchKernelGGL((dkdv_kernel<D, false>), grid_kv, dim3(256), 0, s, a);
+    if (D == 128)
+      hipLaunchKernelGGL((dkdv_q2_kernel<D>), grid_kv, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<D, false>), grid_kv, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid_q(bh, (a.m.n + QCfg<D>::BQ - 1) / QCfg<D>::BQ);

@@ -144,7 +144,7 @@ size_t fa_bwd_workspace_bytes(const fa_params* params);
  * "FlashAttention backward", "The loop structure").  lse: L from fa_fwd;
  * delta: D from fa_bwd_preprocess.  dq_acc: required when deterministic == 0
  * and zeroed by fa_bwd_preprocess beforehand; ignored (may be NULL)
- * otherwise.  dK and dV never depend on the mode. */
+ * otherwise.  dK and dV are bit-reproducible run to run in both modes. */
 fa_status fa_bwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor dout, const float* lse, const float* delta,
                  fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc,
