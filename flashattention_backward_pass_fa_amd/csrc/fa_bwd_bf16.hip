@@ -541,7 +541,9 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.m.n;
-  const int q0 = blockIdx.y * C::BQ;
+  // Longest first: with a causal mask the last query blocks see the most keys.
+  const int qblk = a.m.causal ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+  const int q0 = qblk * C::BQ;
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
   const int64_t row_base = (int64_t)bh * N;
