@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int64_t kMaxSeq = 1 << 24;
+constexpr int64_t kMaxSeq = 1 << 21;  // keeps every launch within 65535 blocks per grid row
 
 // Last HIP error seen by a call on this thread (diagnostics only).
 thread_local int g_last_hip_error = 0;
@@ -29,6 +29,8 @@ fa_status check_params(const fa_params* p) {
   if (p->batch < 1 || p->heads < 1 || p->seqlen < 1 || p->head_dim < 1) return FA_ERR_INVALID_VALUE;
   if ((int64_t)p->batch * p->heads > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
   if (p->seqlen > kMaxSeq) return FA_ERR_NOT_SUPPORTED;
+  // the kernels number their workgroups (one per head and 64 rows) in an int
+  if ((int64_t)p->batch * p->heads * ((p->seqlen + 63) / 64) > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
   if (p->dtype == FA_DTYPE_BF16 && p->head_dim != 64 && p->head_dim != 128) return FA_ERR_NOT_SUPPORTED;
   if (p->dtype == FA_DTYPE_F32 && p->head_dim > 128) return FA_ERR_NOT_SUPPORTED;
   if (!std::isfinite(p->sm_scale)) return FA_ERR_INVALID_VALUE;
@@ -40,6 +42,10 @@ fa_status check_params(const fa_params* p) {
   }
   return FA_SUCCESS;
 }
+
+// Atomic dQ mode (bf16, deterministic == 0) accumulates dQ in an fp32
+// workspace; every other call has none.
+bool uses_dq_acc(const fa_params* p) { return p->dtype == FA_DTYPE_BF16 && !p->deterministic; }
 
 fa_status check_tensor(const fa_params* p, const fa_tensor& t) {
   if (!t.ptr) return FA_ERR_INVALID_VALUE;
@@ -158,7 +164,7 @@ fa_status fa_fwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
 
 size_t fa_bwd_workspace_bytes(const fa_params* p) {
   if (check_params(p) != FA_SUCCESS) return 0;
-  if (p->deterministic) return 0;
+  if (!uses_dq_acc(p)) return 0;
   return (size_t)4 * (size_t)p->batch * (size_t)p->heads * (size_t)p->seqlen * (size_t)p->head_dim;
 }
 
@@ -168,6 +174,8 @@ fa_status fa_bwd_preprocess(const fa_params* p, fa_tensor o, fa_tensor dout, flo
   FA_TRY(check_tensor(p, o));
   FA_TRY(check_tensor(p, dout));
   FA_TRY(check_vec(delta, 4));
+  // the accumulator exists only in atomic mode; any other pointer is ignored
+  if (!uses_dq_acc(p)) dq_acc = nullptr;
   if (dq_acc) FA_TRY(check_vec(dq_acc, 16));
   if ((void*)delta == o.ptr || (void*)delta == dout.ptr || (dq_acc && (void*)dq_acc == (void*)delta))
     return FA_ERR_INVALID_VALUE;
@@ -198,7 +206,7 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   FA_TRY(check_tensor(p, dv));
   FA_TRY(check_vec(lse, 4));
   FA_TRY(check_vec(delta, 4));
-  const bool atomic = p->dtype == FA_DTYPE_BF16 && !p->deterministic;
+  const bool atomic = uses_dq_acc(p);
   if (atomic) FA_TRY(check_vec(dq_acc, 16));
   const void* ins[] = {q.ptr, k.ptr, v.ptr, dout.ptr, lse, delta};
   void* outs[] = {dq.ptr, dk.ptr, dv.ptr, atomic ? (void*)dq_acc : nullptr};

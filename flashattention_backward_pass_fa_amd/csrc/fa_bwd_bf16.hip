@@ -147,10 +147,10 @@ __global__ void __launch_bounds__(256, (kv_min_blocks<D, ATOMIC>())) dkdv_kernel
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.m.n;
-  const int kv0 = blockIdx.y * C::BC;
+  const int kv0 = blk * C::BC;
   const int kvw = kv0 + 32 * w;
   const int key = kvw + c;  // this lane's key (column of S)
 
@@ -385,10 +385,10 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int grp = w & 3, qh = w >> 2;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.m.n;
-  const int kv0 = blockIdx.y * C::BC;
+  const int kv0 = blk * C::BC;
   const int kvw = kv0 + 32 * grp;
   const int key = kvw + c;
 
@@ -538,11 +538,11 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.m.n;
   // Longest first: with a causal mask the last query blocks see the most keys.
-  const int qblk = a.m.causal ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+  const int qblk = a.m.causal ? gridDim.y - 1 - blk : blk;
   const int q0 = qblk * C::BQ;
   const int qw = q0 + 32 * w;
   const int myq = qw + c;

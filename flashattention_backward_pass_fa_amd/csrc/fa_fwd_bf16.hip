@@ -46,10 +46,11 @@ __global__ void __launch_bounds__(256, 1) fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.m.n;
-  const int q0 = blockIdx.y * C::BQ;
+  // Longest first: with a causal mask the last query blocks see the most keys.
+  const int q0 = (a.m.causal ? gridDim.y - 1 - blk : blk) * C::BQ;
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
 

@@ -78,7 +78,8 @@ typedef struct fa_tensor {
 /* Flags and sizes of one attention call.
  *   dtype         FA_DTYPE_F32 or FA_DTYPE_BF16
  *   batch, heads  B, H >= 1
- *   seqlen        N >= 1 (queries and keys have the same length)
+ *   seqlen        1 <= N <= 2^21 (queries and keys have the same length);
+ *                 B * H * ceil(N / 64) must stay below 2^31
  *   head_dim      d: bf16 supports 64 and 128; fp32 supports 1..128
  *   sm_scale      S = sm_scale * Q K^T (the pages use 1/sqrt(d)); any finite
  *                 value, 0 included
@@ -131,20 +132,23 @@ fa_status fa_fwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
 /* Backward pre-pass: D_i = sum_k dO_ik * O_ik, one fp32 scalar per row,
  * accumulated in fp32 ("FlashAttention backward", "The gradients, and the
  * one scalar that makes them local").  delta: fp32 [B,H,N] output.
- * dq_acc: NULL, or the fp32 workspace of fa_bwd (fa_bwd_workspace_bytes),
- * which this call then zeroes; atomic mode requires that. */
+ * dq_acc: the fp32 workspace of fa_bwd when fa_bwd_workspace_bytes(params)
+ * is not 0 (bf16 with deterministic == 0), which this call then zeroes and
+ * which that fa_bwd requires zeroed; NULL there skips the zeroing.  For
+ * every other params it is ignored and never written (may be NULL). */
 fa_status fa_bwd_preprocess(const fa_params* params, fa_tensor o, fa_tensor dout,
                             float* delta, float* dq_acc, void* stream);
 
-/* Bytes of fp32 workspace fa_bwd needs: 4*B*H*N*d when deterministic == 0
- * (the dQ accumulator, [B,H,N,d] contiguous), else 0. */
+/* Bytes of fp32 workspace fa_bwd needs: 4*B*H*N*d for bf16 with
+ * deterministic == 0 (the dQ accumulator, [B,H,N,d] contiguous), else 0
+ * (also 0 when params are invalid). */
 size_t fa_bwd_workspace_bytes(const fa_params* params);
 
 /* Backward: dQ, dK, dV in the input dtype ("Lecture 7", "The math";
  * "FlashAttention backward", "The loop structure").  lse: L from fa_fwd;
- * delta: D from fa_bwd_preprocess.  dq_acc: required when deterministic == 0
- * and zeroed by fa_bwd_preprocess beforehand; ignored (may be NULL)
- * otherwise.  dK and dV are bit-reproducible run to run in both modes. */
+ * delta: D from fa_bwd_preprocess.  dq_acc: required when
+ * fa_bwd_workspace_bytes(params) is not 0, zeroed by fa_bwd_preprocess
+ * beforehand; ignored (may be NULL) otherwise.  dK and dV are bit-reproducible run to run in both modes. */
 fa_status fa_bwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor dout, const float* lse, const float* delta,
                  fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc,

@@ -93,6 +93,8 @@ VOID = ctypes.c_void_p
     (dict(dropout_p=-0.1), 1),
     (dict(dropout_p=math.nan), 1),
     (dict(shape=(1, 1, 70000, 64), dropout_p=0.1), 2),   # dropout counter holds 16-bit indices
+    (dict(shape=(1, 1, (1 << 21) + 1, 64)), 2),           # longest sequence is 2^21
+    (dict(shape=(1 << 16, 1 << 12, 1 << 10, 64)), 2),     # workgroup count past 2^31
 ])
 def test_invalid_params_rejected(lib, mutate, status):
     p = _params(**mutate)
@@ -134,6 +136,8 @@ def test_workspace_bytes(lib):
     p = _params(shape=(2, 3, 100, 128), deterministic=True)
     assert fa.fa_bwd_workspace_bytes(p) == 0
     assert fa.fa_bwd_workspace_bytes(_params(dtype=9)) == 0
+    # fp32 never takes the atomic dQ path
+    assert fa.fa_bwd_workspace_bytes(_params(shape=(2, 3, 100, 128), dtype=fa.FA_DTYPE_F32)) == 0
 
 
 def _no_gpu():

@@ -112,3 +112,30 @@ def test_isolated_backward_from_oracle_forward():
     gpu = case.run_gpu(dev, o=o, lse=lse)
     for name in ("dq", "dk", "dv"):
         assert_close(name, to_host(gpu[name]), ref[name], "bf16")
+
+
+@pytest.mark.parametrize("dtype,deterministic", [("bf16", True), ("f32", False), ("bf16", False)])
+def test_preprocess_writes_workspace_only_in_atomic_mode(dtype, deterministic):
+    """fa_bwd_preprocess zeroes dq_acc in atomic mode and leaves it alone otherwise.
+
+    The buffer is full size in every case, so a wrong write lands in bounds and
+    shows up as changed values."""
+    import ctypes
+    import torch
+    from flashattention_backward_pass_fa_amd import binding as fa
+    case = Case(1, 2, 96, 64, dtype, causal=True, seed=7)
+    print(f"\n[gpu] preprocess workspace {case} deterministic={deterministic}", flush=True)
+    dev = case.device_inputs(case.host_inputs())
+    code = fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F32
+    params = fa.make_params(case.shape, code, causal=True, deterministic=deterministic)
+    ws = torch.full((1 * 2 * 96 * 64,), 7.0, dtype=torch.float32, device="cuda")
+    delta = torch.empty((1, 2, 96), dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    o = dev["q"]  # any [B, H, N, d] tensor stands in for O here
+    assert fa.fa_bwd_preprocess(params, fa.tensor_arg(o), fa.tensor_arg(dev["do"]),
+                                ctypes.c_void_p(delta.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                st) == 0
+    torch.cuda.synchronize()
+    used = fa.fa_bwd_workspace_bytes(params) > 0
+    assert used == (dtype == "bf16" and not deterministic)
+    assert torch.all(ws == (0.0 if used else 7.0)).item()
