@@ -53,6 +53,7 @@ fa_status check_tensor(const fa_params* p, const fa_tensor& t) {
   if (p->dtype == FA_DTYPE_BF16) {
     if (!aligned(t.ptr, 16)) return FA_ERR_MISALIGNED;
     if ((t.stride_b % 8) || (t.stride_h % 8) || (t.stride_n % 8)) return FA_ERR_MISALIGNED;
+    if (t.stride_n > INT32_MAX) return FA_ERR_NOT_SUPPORTED;  // row offsets are 32-bit products
   } else if (!aligned(t.ptr, 4)) {
     return FA_ERR_MISALIGNED;
   }

@@ -1,29 +1,36 @@
 // fa_bwd_bf16.hip - bf16 FlashAttention backward for gfx950 (MFMA 32x32x16).
 //
-// Two kernels ("FlashAttention backward", section "The loop structure"):
+// The backward as a KV-outer and a Q-outer pass ("FlashAttention backward",
+// section "The loop structure"):
 //
-//  dkdv_kernel  KV-outer: one workgroup owns 128 keys (32 per wave) of one
-//               (b, h) and loops over the query blocks that can see them.
-//               For each 64-query block it recomputes S = Q K^T and
-//               dP = dO V^T on MFMA, rebuilds P = exp(S - L) from the saved
-//               LSE ("Lecture 7", "The recomputation trick"), forms
-//               dS = P * (dP - D) with the pre-pass scalar D, and
-//               accumulates dV += P~^T dO and dK += dS^T Q in fp32
-//               registers, written once at the end.  In atomic mode it also
-//               adds dS K into an fp32 dQ accumulator with device atomics.
-//  dq_kernel    Q-outer: one workgroup owns 128 queries (32 per wave) and
-//               loops over the visible key blocks, recomputing S, P, dP, dS
-//               to accumulate dQ = dS K in registers: the deterministic,
-//               atomic-free dQ.
+//  dkdv_kernel     KV-outer, 4 waves: one workgroup owns 128 keys (32 per
+//                  wave, K and V in registers) of one (b, h) and loops over
+//                  the 64-query blocks that can see them.  For each it
+//                  recomputes S = Q K^T and dP = dO V^T on MFMA, rebuilds
+//                  P = exp(S - L) from the saved LSE ("Lecture 7", "The
+//                  recomputation trick"), forms dS = P * (dP - D) with the
+//                  pre-pass scalar D, and accumulates dV += P~^T dO and
+//                  dK += dS^T Q in fp32 registers, written once at the end.
+//                  In atomic mode it also adds dS K into an fp32 dQ
+//                  accumulator with device atomics.
+//  dkdv_q2_kernel  KV-outer, 8 waves (two per SIMD) for d = 128: the same
+//                  work with K and V in LDS and each query block split
+//                  between two waves per key group.
+//  dq_kernel       Q-outer: one workgroup owns 128 queries (32 per wave) and
+//                  streams 32-key blocks through a ring of three LDS
+//                  buffers, recomputing S, P, dP, dS to accumulate dQ = dS K
+//                  in registers: the deterministic, atomic-free dQ.
 //
-// Layout in LDS: Q, dO (and K, V in dq_kernel) tiles are row-major bf16 with
-// a 16-element pad per row.  The k-inside-lane operands of the dV/dK/dQ
-// products are read from those same tiles with ds_read_tr16_b64, so no
-// transposed copies are kept.  K and V of the wave's own keys live in
-// registers for the whole kernel (B operand of S and dP).
-// Blocks that are fully masked (causal/window) are never visited; a wave
-// whose 64x32 sub-tile is fully masked skips its products; only tiles that
-// straddle a mask edge or the sequence end evaluate the per-element mask.
+// Layout in LDS: Q, dO, K, V tiles are row-major bf16 with a padded row
+// stride.  The k-inside-lane operands of the dV/dK/dQ products are read
+// from those same tiles with ds_read_tr16_b64, so no transposed copies are
+// kept.  Blocks that are fully masked (causal/window) are never visited; a
+// wave whose 32x32 tile is fully masked skips its products; only tiles that
+// straddle a mask edge or the sequence end evaluate the per-element mask,
+// and the fully visible ones run a path ordered so that the exponentials
+// and dS sit beside independent MFMAs.
+
+#include <type_traits>
 
 #include "fa_kernels.h"
 
@@ -53,17 +60,6 @@ struct KvCfg {
 template <int D, bool ATOMIC>
 constexpr int kv_min_blocks() { return (D == 64 && !ATOMIC) ? 2 : (D == 128 && !ATOMIC ? KV_MINB_128 : 1); }
 
-template <int D>
-struct QCfg {
-  static constexpr int BQ = 128;          // queries per workgroup
-  static constexpr int BK = 64;           // keys per inner iteration
-  static constexpr int NT = 256;
-  static constexpr int LD = lds_stride(D);
-  static constexpr int KT = D / 16;
-  static constexpr int DT = D / 32;
-  static constexpr int CH = D / 8;
-  static constexpr int LOADS = BK * CH / NT;
-};
 
 __device__ __forceinline__ bf16x8 load8(const bf16* p) { return *(const bf16x8*)p; }
 __device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *(bf16x8*)p = v; }
@@ -130,6 +126,64 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
         da1[r - 8] = (bf16)ds;
       }
     }
+  }
+}
+
+// One fully visible 32-query x 32-key tile of a KV-outer wave, without
+// dropout, ordered so that VALU work has independent MFMAs beside it: S,
+// then dP while P = exp2(S c - L) is formed, then dV += P^T dO while
+// dS = P (dP - D) is formed, then dK += dS^T Q.  qrow/orow point at this
+// lane's query row of the Q and dO tiles (at column 8 g), kr/vr at its key
+// row of K and V; u0 is the first 16-query k-step of the tile.
+template <int D, int LD>
+__device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow, const bf16* orow,
+                                             const bf16* kr, const bf16* vr, const bf16* Qs,
+                                             const bf16* Os, const float* sLq, const float* sDq,
+                                             int g, int lane, int u0, f32x16* dk_acc,
+                                             f32x16* dv_acc) {
+  constexpr int KT = D / 16, DT = D / 32;
+  f32x16 sacc = f32x16{};
+#pragma unroll
+  for (int t = 0; t < KT; ++t) sacc = mfma32x32x16(load8(qrow + 16 * t), load8(kr + 16 * t), sacc);
+  f32x16 dpacc = f32x16{};
+#pragma unroll
+  for (int t = 0; t < KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), load8(vr + 16 * t), dpacc);
+  float p[16];
+  bf16x8 pa[2], da[2];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * rr + e;
+      p[r] = fast_exp2(sacc[r] * a.scale_log2 - l4[e]);
+      pa[r >> 3][r & 7] = (bf16)p[r];
+    }
+  }
+#pragma unroll
+  for (int u2 = 0; u2 < 2; ++u2) {
+    const int u = u0 + u2;
+#pragma unroll
+    for (int n = 0; n < DT; ++n)
+      dv_acc[n] = mfma32x32x16(pa[u2], tr_operand(Os, LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane),
+                               dv_acc[n]);
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const f32x4 d4 = *(const f32x4*)(sDq + 8 * rr + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * rr + e;
+      da[r >> 3][r & 7] = (bf16)(p[r] * (dpacc[r] - d4[e]));
+    }
+  }
+#pragma unroll
+  for (int u2 = 0; u2 < 2; ++u2) {
+    const int u = u0 + u2;
+#pragma unroll
+    for (int n = 0; n < DT; ++n)
+      dk_acc[n] = mfma32x32x16(da[u2], tr_operand(Qs, LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane),
+                               dk_acc[n]);
   }
 }
 
@@ -410,6 +464,9 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   }
 
   const int64_t row_base = (int64_t)bh * N;
+  const char* q_head = (const char*)at<bf16>(a.q, b, h, 0);
+  const char* o_head = (const char*)at<bf16>(a.dout, b, h, 0);
+  const uint32_t q_rs = (uint32_t)a.q.sn * 2, o_rs = (uint32_t)a.dout.sn * 2;
   bf16x8 pq[C::LOADS], po[C::LOADS];
   float pld = 0.f;
   auto load_tile = [&](int it) {
@@ -419,8 +476,8 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int qr = min(q0 + row, N - 1);
-      pq[x] = load8(at<bf16>(a.q, b, h, qr) + col);
-      po[x] = load8(at<bf16>(a.dout, b, h, qr) + col);
+      pq[x] = load8((const bf16*)row_addr(q_head, q_rs, qr) + col);
+      po[x] = load8((const bf16*)row_addr(o_head, o_rs, qr) + col);
     }
     if (tid < 2 * C::BR) {
       const int qr = q0 + (tid & (C::BR - 1));
@@ -454,14 +511,18 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
 
   const bf16* Kr = sK + (32 * grp + c) * C::LD + 8 * g;  // this lane's key row (B operands)
   const bf16* Vr = sV + (32 * grp + c) * C::LD + 8 * g;
-  for (int it = it0; it < it1; ++it) {
+  auto step = [&](int it, auto full) {
     const int buf = (it - it0) & 1;
     const bool has_next = it + 1 < it1;
     if (has_next) load_tile(it + 1);
     const bf16* Qs = smem + buf * TILE;
     const bf16* Os = smem + (2 + buf) * TILE;
     const int qs = it * C::BR + 32 * qh;
-    if (!block_dead(a.m, qs, 32, kvw, 32)) {
+    if (decltype(full)::value) {
+      kv_full_tile<D, C::LD>(a, Qs + (32 * qh + c) * C::LD + 8 * g, Os + (32 * qh + c) * C::LD + 8 * g, Kr,
+                             Vr, Qs, Os, &sL[buf][32 * qh], &sD[buf][32 * qh], g, lane, 2 * qh, dk_acc,
+                             dv_acc);
+    } else if (!block_dead(a.m, qs, 32, kvw, 32)) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int t = 0; t < C::KT; ++t) {
@@ -473,10 +534,7 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
       bf16x8 pa0, pa1, da0, da1;
       const float* sLq = &sL[buf][32 * qh];
       const float* sDq = &sD[buf][32 * qh];
-      if (block_full(a.m, qs, 32, kvw, 32) && !a.m.dropout)
-        kv_elementwise<false>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
-      else
-        kv_elementwise<true>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
+      kv_elementwise<true>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         const int u = 2 * qh + u2;
@@ -495,7 +553,24 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     }
     if (has_next) store_tile(buf ^ 1);
     lds_barrier();
+  };
+  int itA = it1, itB = it1;
+  if (!a.m.dropout && kv0 + C::BC <= N) {
+    int lo = 0, hi = N - C::BR;
+    if (a.m.causal) lo = max(lo, kv0 + C::BC - 1);
+    if (a.m.wr >= 0) lo = max(lo, kv0 + C::BC - 1 - a.m.wr);
+    if (a.m.wl >= 0) hi = min(hi, kv0 - C::BR + 1 + a.m.wl);
+    if (lo <= hi) {
+      itA = min(max(it0, (lo + C::BR - 1) / C::BR), it1);
+      itB = max(itA, min(it1, hi / C::BR + 1));
+    }
   }
+  std::integral_constant<bool, false> general;
+  std::integral_constant<bool, true> fast;
+  int it = it0;
+  for (; it < itA; ++it) step(it, general);
+  for (; it < itB; ++it) step(it, fast);
+  for (; it < it1; ++it) step(it, general);
 
   // Sum the two query halves of each key group: waves 4..7 hand their
   // partials to waves 0..3 through LDS (value r of tile n of lane l at
@@ -530,11 +605,27 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- Q-outer
 
+// Q-outer dQ kernel with 32-key blocks streamed through a ring of three LDS
+// buffers, so that one block's S^T, dP^T products can run while the previous
+// block's dS is formed.  Block j + 2 is loaded into registers while block j
+// is worked on and lands in the buffer block j - 1 used.  Over key blocks
+// that the whole workgroup sees without a mask edge (and without dropout)
+// each iteration issues S^T, dP^T of block j + 1 beside the exponentials and
+// dS of block j, then dQ += dS K of block j; other blocks run the plain
+// per-block sequence with the mask.
+template <int D>
+struct QCfg {
+  static constexpr int BQ = 128, BK = 32, NT = 256;
+  static constexpr int LD = lds_stride(D);
+  static constexpr int KT = D / 16, DT = D / 32, CH = D / 8;
+  static constexpr int LOADS = BK * CH / NT;
+};
+
 template <int D>
 __global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][C::BK * C::LD];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) bf16 sK[3][C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) bf16 sV[3][C::BK * C::LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
@@ -570,6 +661,9 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
   const int jt0 = k_lo / C::BK;
   const int jt1 = k_lo < k_hi ? (k_hi + C::BK - 1) / C::BK : jt0;
 
+  const char* k_head = (const char*)at<bf16>(a.k, b, h, 0);
+  const char* v_head = (const char*)at<bf16>(a.v, b, h, 0);
+  const uint32_t k_rs = (uint32_t)a.k.sn * 2, v_rs = (uint32_t)a.v.sn * 2;
   bf16x8 pk[C::LOADS], pv[C::LOADS];
   auto load_tile = [&](int jt) {
     const int k0 = jt * C::BK;
@@ -577,14 +671,9 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int kr = k0 + row;
-      if (kr < N) {
-        pk[x] = load8(at<bf16>(a.k, b, h, kr) + col);
-        pv[x] = load8(at<bf16>(a.v, b, h, kr) + col);
-      } else {
-        pk[x] = zero8();
-        pv[x] = zero8();
-      }
+      const int kr = min(k0 + row, N - 1);  // rows past the end are masked: read a valid one
+      pk[x] = load8((const bf16*)row_addr(k_head, k_rs, kr) + col);
+      pv[x] = load8((const bf16*)row_addr(v_head, v_rs, kr) + col);
     }
   };
   auto store_tile = [&](int buf) {
@@ -596,67 +685,115 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
       store8(&sV[buf][row * C::LD + col], pv[x]);
     }
   };
+  auto ring = [&](int jt) { return (jt - jt0) % 3; };
 
   f32x16 dq_acc[C::DT];
 #pragma unroll
   for (int n = 0; n < C::DT; ++n) dq_acc[n] = f32x16{};
 
+  // S^T, dP^T of one 32-key block against this wave's queries
+  auto sdp = [&](int buf, f32x16& st, f32x16& dpt) {
+    st = f32x16{};
+    dpt = f32x16{};
+#pragma unroll
+    for (int t = 0; t < C::KT; ++t) {
+      st = mfma32x32x16(load8(&sK[buf][c * C::LD + 16 * t + 8 * g]), qreg[t], st);
+      dpt = mfma32x32x16(load8(&sV[buf][c * C::LD + 16 * t + 8 * g]), oreg[t], dpt);
+    }
+  };
+  auto dqmm = [&](int buf, const bf16x8& d0, const bf16x8& d1) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int n = 0; n < C::DT; ++n)
+        dq_acc[n] = mfma32x32x16(u ? d1 : d0, tr_operand(sK[buf], C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane),
+                                 dq_acc[n]);
+    }
+  };
+  // the end of every iteration: publish block jt + 2, wait for all waves
+  auto advance = [&](int jt) {
+    if (jt + 2 < jt1) store_tile(ring(jt + 2));
+    lds_barrier();
+  };
+
   if (jt0 < jt1) {
     load_tile(jt0);
     store_tile(0);
+    if (jt0 + 1 < jt1) {
+      load_tile(jt0 + 1);
+      store_tile(1);
+    }
   }
   __syncthreads();
 
-  for (int jt = jt0; jt < jt1; ++jt) {
-    const int buf = (jt - jt0) & 1;
-    const bool has_next = jt + 1 < jt1;
-    if (has_next) load_tile(jt + 1);
-    const bf16* Ks = sK[buf];
-    const bf16* Vs = sV[buf];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int ks = jt * C::BK + 32 * kt;  // first key of this 32-key sub-tile
-      if (block_dead(a.m, qw, 32, ks, 32)) continue;
-      bf16x8 ak[C::KT], av[C::KT];
-#pragma unroll
-      for (int t = 0; t < C::KT; ++t) {
-        ak[t] = load8(Ks + (32 * kt + c) * C::LD + 16 * t + 8 * g);
-        av[t] = load8(Vs + (32 * kt + c) * C::LD + 16 * t + 8 * g);
-      }
-      f32x16 st = f32x16{}, dpt = f32x16{};
-#pragma unroll
-      for (int t = 0; t < C::KT; ++t) {
-        st = mfma32x32x16(ak[t], qreg[t], st);
-        dpt = mfma32x32x16(av[t], oreg[t], dpt);
-      }
-      bf16x8 da0, da1;
-      const bool general = !block_full(a.m, qw, 32, ks, 32) || a.m.dropout;
+  // Key blocks [jtA, jtB) are seen by all 128 queries of the block with no
+  // mask edge and no dropout.
+  int jtA = jt1, jtB = jt1;
+  if (!a.m.dropout && q0 + C::BQ <= N) {
+    int lo = 0, hi = N - C::BK;
+    if (a.m.causal) hi = min(hi, q0 - C::BK + 1);
+    if (a.m.wr >= 0) hi = min(hi, q0 + a.m.wr - C::BK + 1);
+    if (a.m.wl >= 0) lo = max(lo, q0 + C::BQ - 1 - a.m.wl);
+    if (lo <= hi) {
+      jtA = min(max(jt0, (lo + C::BK - 1) / C::BK), jt1);
+      jtB = max(jtA, min(jt1, hi / C::BK + 1));
+    }
+  }
+
+  auto general = [&](int jt) {
+    if (jt + 2 < jt1) load_tile(jt + 2);
+    const int buf = ring(jt);
+    const int ks = jt * C::BK;
+    if (!block_dead(a.m, qw, 32, ks, 32)) {
+      f32x16 st, dpt;
+      sdp(buf, st, dpt);
+      bf16x8 d0, d1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        const int kr = ks + 8 * (r >> 2) + 4 * g + (r & 3);
         float p = fast_exp2(st[r] * a.scale_log2 - l2);
         float dpv = dpt[r];
-        if (general) {
-          const int kr = ks + 8 * (r >> 2) + 4 * g + (r & 3);
-          p = visible(a.m, myq, kr) ? p : 0.f;
-          if (a.m.dropout) dpv = dropout_keep(a.m, b, h, myq, kr) ? dpv * a.m.keep_scale : 0.f;
-        }
+        p = visible(a.m, myq, kr) ? p : 0.f;
+        if (a.m.dropout) dpv = dropout_keep(a.m, b, h, myq, kr) ? dpv * a.m.keep_scale : 0.f;
         const bf16 v = (bf16)(p * (dpv - dd));
-        if (r < 8) da0[r] = v; else da1[r - 8] = v;
+        if (r < 8) d0[r] = v; else d1[r - 8] = v;
       }
-#pragma unroll
-      for (int u2 = 0; u2 < 2; ++u2) {
-        const int u = 2 * kt + u2;
-        bf16x8 bk[C::DT];
-#pragma unroll
-        for (int n = 0; n < C::DT; ++n)
-          bk[n] = tr_operand(Ks, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
-#pragma unroll
-        for (int n = 0; n < C::DT; ++n) dq_acc[n] = mfma32x32x16(u2 ? da1 : da0, bk[n], dq_acc[n]);
-      }
+      dqmm(buf, d0, d1);
     }
-    if (has_next) store_tile(buf ^ 1);
-    lds_barrier();
+    advance(jt);
+  };
+
+  int jt = jt0;
+  for (; jt < jtA; ++jt) general(jt);
+  if (jtA < jtB) {
+    auto ds_of = [&](const f32x16& st, const f32x16& dpt, bf16x8& d0, bf16x8& d1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bf16 v = (bf16)(fast_exp2(st[r] * a.scale_log2 - l2) * (dpt[r] - dd));
+        if (r < 8) d0[r] = v; else d1[r - 8] = v;
+      }
+    };
+    f32x16 st, dpt;
+    sdp(ring(jtA), st, dpt);
+    for (; jt + 1 < jtB; ++jt) {
+      if (jt + 2 < jt1) load_tile(jt + 2);
+      f32x16 st_n, dpt_n;
+      sdp(ring(jt + 1), st_n, dpt_n);
+      bf16x8 d0, d1;
+      ds_of(st, dpt, d0, d1);
+      dqmm(ring(jt), d0, d1);
+      advance(jt);
+      st = st_n;
+      dpt = dpt_n;
+    }
+    if (jt + 2 < jt1) load_tile(jt + 2);
+    bf16x8 d0, d1;
+    ds_of(st, dpt, d0, d1);
+    dqmm(ring(jt), d0, d1);
+    advance(jt);
+    ++jt;
   }
+  for (; jt < jt1; ++jt) general(jt);
 
 #pragma unroll
   for (int n = 0; n < C::DT; ++n) {

@@ -137,6 +137,12 @@ __device__ __forceinline__ bool dropout_keep(const MaskArgs& m, int b, int h, in
   return x >= m.keep_threshold;
 }
 
+// Address of row `row` (0 <= row < 2^31) of one head whose rows are `rs`
+// bytes apart (rs < 2^32): a single 32 x 32 -> 64-bit multiply-add.
+__device__ __forceinline__ const char* row_addr(const char* head, uint32_t rs, int row) {
+  return head + (uint64_t)(uint32_t)row * rs;
+}
+
 template <typename T>
 __device__ __forceinline__ T* at(const TensorView& t, int b, int h, int n) {
   return (T*)t.ptr + (int64_t)b * t.sb + (int64_t)h * t.sh + (int64_t)n * t.sn;

@@ -45,7 +45,8 @@ __global__ void __launch_bounds__(256, 1) fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sV[2][C::BK * C::LD];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  // the wave index is uniform across the wave: keep it (and all derived from it) scalar
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), c = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.m.n;
