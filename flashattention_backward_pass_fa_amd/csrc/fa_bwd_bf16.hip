@@ -142,12 +142,16 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
                                              int g, int lane, int u0, f32x16* dk_acc,
                                              f32x16* dv_acc) {
   constexpr int KT = D / 16, DT = D / 32;
+  const int ulo = 16 * u0 + 4 * g;  // first query row of this lane's k-steps
   f32x16 sacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) sacc = mfma32x32x16(load8(qrow + 16 * t), load8(kr + 16 * t), sacc);
   f32x16 dpacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), load8(vr + 16 * t), dpacc);
+  bf16x8 b0[DT], b1[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) b0[n] = tr_operand(Os, LD, ulo, ulo + 8, 32 * n, lane);
   float p[16];
   bf16x8 pa[2], da[2];
 #pragma unroll
@@ -161,13 +165,13 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
     }
   }
 #pragma unroll
-  for (int u2 = 0; u2 < 2; ++u2) {
-    const int u = u0 + u2;
+  for (int n = 0; n < DT; ++n) b1[n] = tr_operand(Os, LD, ulo + 16, ulo + 24, 32 * n, lane);
 #pragma unroll
-    for (int n = 0; n < DT; ++n)
-      dv_acc[n] = mfma32x32x16(pa[u2], tr_operand(Os, LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane),
-                               dv_acc[n]);
-  }
+  for (int n = 0; n < DT; ++n) dv_acc[n] = mfma32x32x16(pa[0], b0[n], dv_acc[n]);
+#pragma unroll
+  for (int n = 0; n < DT; ++n) dv_acc[n] = mfma32x32x16(pa[1], b1[n], dv_acc[n]);
+#pragma unroll
+  for (int n = 0; n < DT; ++n) b0[n] = tr_operand(Qs, LD, ulo, ulo + 8, 32 * n, lane);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4 d4 = *(const f32x4*)(sDq + 8 * rr + 4 * g);
@@ -178,13 +182,11 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
     }
   }
 #pragma unroll
-  for (int u2 = 0; u2 < 2; ++u2) {
-    const int u = u0 + u2;
+  for (int n = 0; n < DT; ++n) b1[n] = tr_operand(Qs, LD, ulo + 16, ulo + 24, 32 * n, lane);
 #pragma unroll
-    for (int n = 0; n < DT; ++n)
-      dk_acc[n] = mfma32x32x16(da[u2], tr_operand(Qs, LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane),
-                               dk_acc[n]);
-  }
+  for (int n = 0; n < DT; ++n) dk_acc[n] = mfma32x32x16(da[0], b0[n], dk_acc[n]);
+#pragma unroll
+  for (int n = 0; n < DT; ++n) dk_acc[n] = mfma32x32x16(da[1], b1[n], dk_acc[n]);
 }
 
 // ---------------------------------------------------------------- KV-outer
@@ -615,14 +617,15 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
 // per-block sequence with the mask.
 template <int D>
 struct QCfg {
-  static constexpr int BQ = 128, BK = 32, NT = 256;
+  static constexpr int NT = D == 128 ? 512 : 256, BQ = NT / 2, BK = 32;
+  static constexpr int MINB = 512 / NT;
   static constexpr int LD = lds_stride(D);
   static constexpr int KT = D / 16, DT = D / 32, CH = D / 8;
   static constexpr int LOADS = BK * CH / NT;
 };
 
 template <int D>
-__global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sK[3][C::BK * C::LD];
   __shared__ __attribute__((aligned(16))) bf16 sV[3][C::BK * C::LD];
@@ -779,9 +782,18 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(BwdArgs a) {
       if (jt + 2 < jt1) load_tile(jt + 2);
       f32x16 st_n, dpt_n;
       sdp(ring(jt + 1), st_n, dpt_n);
+      const bf16* Kc = sK[ring(jt)];
+      bf16x8 b0[C::DT], b1[C::DT];
+#pragma unroll
+      for (int n = 0; n < C::DT; ++n) b0[n] = tr_operand(Kc, C::LD, 4 * g, 8 + 4 * g, 32 * n, lane);
       bf16x8 d0, d1;
       ds_of(st, dpt, d0, d1);
-      dqmm(ring(jt), d0, d1);
+#pragma unroll
+      for (int n = 0; n < C::DT; ++n) b1[n] = tr_operand(Kc, C::LD, 16 + 4 * g, 24 + 4 * g, 32 * n, lane);
+#pragma unroll
+      for (int n = 0; n < C::DT; ++n) dq_acc[n] = mfma32x32x16(d0, b0[n], dq_acc[n]);
+#pragma unroll
+      for (int n = 0; n < C::DT; ++n) dq_acc[n] = mfma32x32x16(d1, b1[n], dq_acc[n]);
       advance(jt);
       st = st_n;
       dpt = dpt_n;
@@ -817,7 +829,7 @@ hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid_q(bh, (a.m.n + QCfg<D>::BQ - 1) / QCfg<D>::BQ);
-    hipLaunchKernelGGL((dq_kernel<D>), grid_q, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((dq_kernel<D>), grid_q, dim3(QCfg<D>::NT), 0, s, a);
   } else {
     hipLaunchKernelGGL((dkdv_kernel<D, true>), grid_kv, dim3(256), 0, s, a);
   }
