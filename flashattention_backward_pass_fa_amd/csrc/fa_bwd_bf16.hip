@@ -135,17 +135,18 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
 // dS = P (dP - D) is formed, then dK += dS^T Q.  qrow/orow point at this
 // lane's query row of the Q and dO tiles (at column 8 g), kr/vr at its key
 // row of K and V; u0 is the first 16-query k-step of the tile.
-template <int D, int LD>
+template <int D, int LD, typename Mid>
 __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow, const bf16* orow,
                                              const bf16* kr, const bf16* vr, const bf16* Qs,
                                              const bf16* Os, const float* sLq, const float* sDq,
                                              int g, int lane, int u0, f32x16* dk_acc,
-                                             f32x16* dv_acc) {
+                                             f32x16* dv_acc, Mid mid) {
   constexpr int KT = D / 16, DT = D / 32;
   const int ulo = 16 * u0 + 4 * g;  // first query row of this lane's k-steps
   f32x16 sacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) sacc = mfma32x32x16(load8(qrow + 16 * t), load8(kr + 16 * t), sacc);
+  mid();
   f32x16 dpacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), load8(vr + 16 * t), dpacc);
@@ -513,17 +514,19 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
 
   const bf16* Kr = sK + (32 * grp + c) * C::LD + 8 * g;  // this lane's key row (B operands)
   const bf16* Vr = sV + (32 * grp + c) * C::LD + 8 * g;
-  auto step = [&](int it, auto full) {
+  // FULL: every wave's tile fully visible; PRE: the next block exists and is
+  // loaded from inside the tile's products
+  auto step = [&](int it, auto full, auto pre) {
     const int buf = (it - it0) & 1;
     const bool has_next = it + 1 < it1;
-    if (has_next) load_tile(it + 1);
+    if (!decltype(pre)::value && has_next) load_tile(it + 1);
     const bf16* Qs = smem + buf * TILE;
     const bf16* Os = smem + (2 + buf) * TILE;
     const int qs = it * C::BR + 32 * qh;
     if (decltype(full)::value) {
       kv_full_tile<D, C::LD>(a, Qs + (32 * qh + c) * C::LD + 8 * g, Os + (32 * qh + c) * C::LD + 8 * g, Kr,
                              Vr, Qs, Os, &sL[buf][32 * qh], &sD[buf][32 * qh], g, lane, 2 * qh, dk_acc,
-                             dv_acc);
+                             dv_acc, [&] { if (decltype(pre)::value) load_tile(it + 1); });
     } else if (!block_dead(a.m, qs, 32, kvw, 32)) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
@@ -569,10 +572,13 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   }
   std::integral_constant<bool, false> general;
   std::integral_constant<bool, true> fast;
+  std::integral_constant<bool, false> no_pre;
+  std::integral_constant<bool, true> pre;
   int it = it0;
-  for (; it < itA; ++it) step(it, general);
-  for (; it < itB; ++it) step(it, fast);
-  for (; it < it1; ++it) step(it, general);
+  for (; it < itA; ++it) step(it, general, no_pre);
+  for (; it < min(itB, it1 - 1); ++it) step(it, fast, pre);
+  for (; it < itB; ++it) step(it, fast, no_pre);
+  for (; it < it1; ++it) step(it, general, no_pre);
 
   // Sum the two query halves of each key group: waves 4..7 hand their
   // partials to waves 0..3 through LDS (value r of tile n of lane l at
