@@ -97,6 +97,21 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
                                                const float* sLq, const float* sDq, int g, int b,
                                                int h, int q0, int key, bf16x8& pa0, bf16x8& pa1,
                                                bf16x8& da0, bf16x8& da1) {
+  // Dropout: keys across lanes, so the four lanes of a quad hold the four keys
+  // of one Philox block.  Lane t of the quad draws the blocks of the rows
+  // with e = t (one per rr: bits 4 rr .. 4 rr + 3), and the quad shares them.
+  uint32_t kq[4] = {0xFFFFu, 0xFFFFu, 0xFFFFu, 0xFFFFu};
+  const int t = key & 3;
+  if (GENERAL && a.m.dropout) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      mine |= dropout_keep4(a.m, b, h, q0 + 8 * rr + 4 * g + t, key & ~3) << (4 * rr);
+    kq[0] = __builtin_amdgcn_mov_dpp((int)mine, 0x00, 0xF, 0xF, false);  // quad_perm [0,0,0,0]
+    kq[1] = __builtin_amdgcn_mov_dpp((int)mine, 0x55, 0xF, 0xF, false);  // quad_perm [1,1,1,1]
+    kq[2] = __builtin_amdgcn_mov_dpp((int)mine, 0xAA, 0xF, 0xF, false);  // quad_perm [2,2,2,2]
+    kq[3] = __builtin_amdgcn_mov_dpp((int)mine, 0xFF, 0xF, 0xF, false);  // quad_perm [3,3,3,3]
+  }
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
@@ -112,7 +127,7 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
         p = visible(a.m, qi, key) ? p : 0.f;
         pdrop = p;
         if (a.m.dropout) {
-          const bool keep = dropout_keep(a.m, b, h, qi, key);
+          const bool keep = (kq[e] >> (4 * rr + t)) & 1u;
           pdrop = keep ? p * a.m.keep_scale : 0.f;
           dpv = keep ? dpv * a.m.keep_scale : 0.f;
         }
@@ -758,14 +773,20 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
       sdp(buf, st, dpt);
       bf16x8 d0, d1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = ks + 8 * (r >> 2) + 4 * g + (r & 3);
-        float p = fast_exp2(st[r] * a.scale_log2 - l2);
-        float dpv = dpt[r];
-        p = visible(a.m, myq, kr) ? p : 0.f;
-        if (a.m.dropout) dpv = dropout_keep(a.m, b, h, myq, kr) ? dpv * a.m.keep_scale : 0.f;
-        const bf16 v = (bf16)(p * (dpv - dd));
-        if (r < 8) d0[r] = v; else d1[r - 8] = v;
+      for (int rr = 0; rr < 4; ++rr) {
+        // keys j4 .. j4 + 3 of this lane's query share one dropout block
+        const int j4 = ks + 8 * rr + 4 * g;
+        const uint32_t keep = a.m.dropout ? dropout_keep4(a.m, b, h, myq, j4) : 0xFu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float p = fast_exp2(st[r] * a.scale_log2 - l2);
+          float dpv = dpt[r];
+          p = visible(a.m, myq, j4 + e) ? p : 0.f;
+          if (a.m.dropout) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
+          const bf16 v = (bf16)(p * (dpv - dd));
+          if (r < 8) d0[r] = v; else d1[r - 8] = v;
+        }
       }
       dqmm(buf, d0, d1);
     }

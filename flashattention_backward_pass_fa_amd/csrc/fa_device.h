@@ -108,10 +108,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Philox4x32-10 (Salmon et al., SC'11): word 0 of the block for counter
-// (off_lo, off_hi, (i << 16) | j, (b << 16) | h) under key (seed_lo, seed_hi).
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                                 uint32_t k0, uint32_t k1) {
+// Philox4x32-10 (Salmon et al., SC'11): the four output words of the block
+// for counter (c0, c1, c2, c3) under key (k0, k1).
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
   const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
   const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
@@ -128,13 +128,24 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
     k0 += W0;
     k1 += W1;
   }
-  return c0;
+  return u32x4{c0, c1, c2, c3};
 }
 
+// Dropout keep bits of keys j4 .. j4 + 3 (j4 a multiple of 4) in row i of
+// head (b, h): one Philox block per four consecutive keys, counter
+// (off_lo, off_hi, (i << 16) | j4, (b << 16) | h), key j4 + k kept iff word
+// k >= threshold.  Bit k of the result is key j4 + k.
+__device__ __forceinline__ uint32_t dropout_keep4(const MaskArgs& m, int b, int h, int i, int j4) {
+  const u32x4 x = philox4x32_10(m.off_lo, m.off_hi, ((uint32_t)i << 16) | (uint32_t)j4,
+                                ((uint32_t)b << 16) | (uint32_t)h, m.seed_lo, m.seed_hi);
+  const uint32_t t = m.keep_threshold;
+  return (uint32_t)(x[0] >= t) | ((uint32_t)(x[1] >= t) << 1) | ((uint32_t)(x[2] >= t) << 2) |
+         ((uint32_t)(x[3] >= t) << 3);
+}
+
+// Keep bit of one element (i, j).
 __device__ __forceinline__ bool dropout_keep(const MaskArgs& m, int b, int h, int i, int j) {
-  const uint32_t x = philox_word0(m.off_lo, m.off_hi, ((uint32_t)i << 16) | (uint32_t)j,
-                                  ((uint32_t)b << 16) | (uint32_t)h, m.seed_lo, m.seed_hi);
-  return x >= m.keep_threshold;
+  return (dropout_keep4(m, b, h, i, j & ~3) >> (j & 3)) & 1u;
 }
 
 // Address of row `row` (0 <= row < 2^31) of one head whose rows are `rs`
@@ -148,30 +159,5 @@ __device__ __forceinline__ T* at(const TensorView& t, int b, int h, int n) {
   return (T*)t.ptr + (int64_t)b * t.sb + (int64_t)h * t.sh + (int64_t)n * t.sn;
 }
 
-// This wave's share (of 4 waves) of a direct global->LDS load of rows
-// [row0, row0 + ROWS) of tensor t (D columns) into a padded row-major tile
-// of row stride lds_stride(D).  Each wave-wide 16-byte load fills 1 KB of
-// the tile: lane L supplies the global chunk that belongs at tile byte
-// 1024 kb + 16 L.  Pad slots re-read chunk 0 of their row and rows past the
-// sequence end re-read row n - 1, so the tile only holds finite values.
-template <int D, int ROWS>
-__device__ __forceinline__ void dma_tile(bf16* tile, const TensorView& t, int b, int h, int row0,
-                                         int n, int w, int lane) {
-  constexpr int CPR = lds_stride(D) / 8;  // 16-byte chunks per padded row
-  constexpr int KB = ROWS * CPR / 64;     // wave-wide loads per tile
-  static_assert(ROWS * CPR % 64 == 0, "tile must be a whole number of KB");
-  for (int kb = w; kb < KB; kb += 4) {
-    const int idx = kb * 64 + lane;
-    const int row = idx / CPR, chunk = idx - row * CPR;
-    const int src = min(row0 + row, n - 1);
-    const bf16* gp = at<bf16>(t, b, h, src) + 8 * (chunk < D / 8 ? chunk : 0);
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gp,
-                                     (void FA_LDS*)(tile + kb * 512), 16, 0, 0);
-  }
-}
-
-// Wait until every global load this wave issued (including direct-to-LDS
-// loads) has completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace fa

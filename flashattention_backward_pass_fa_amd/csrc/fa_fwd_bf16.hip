@@ -150,15 +150,19 @@ __global__ void __launch_bounds__(256, 1) fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(st[kt][r] - m_use);
-        l_run += p;
-        float pd = p;
-        if (a.m.dropout) {
-          const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-          pd = dropout_keep(a.m, b, h, myq, key) ? p * a.m.keep_scale : 0.f;
+      for (int rr = 0; rr < 4; ++rr) {
+        // keys j4 .. j4 + 3 of this lane's query share one dropout block
+        const uint32_t keep =
+            a.m.dropout ? dropout_keep4(a.m, b, h, myq, k0 + 32 * kt + 8 * rr + 4 * g) : 0xFu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          const float p = fast_exp2(st[kt][r] - m_use);
+          l_run += p;
+          float pd = p;
+          if (a.m.dropout) pd = (keep >> e) & 1u ? p * a.m.keep_scale : 0.f;
+          pb[2 * kt + (r >> 3)][r & 7] = (bf16)pd;
         }
-        pb[2 * kt + (r >> 3)][r & 7] = (bf16)pd;
       }
     }
     m_run = m_new;

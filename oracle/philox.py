@@ -7,12 +7,13 @@ The dropout rule comes from "Lecture 7 - Backward Pass and Validation",
 section "Dropout": the kernel draws a Bernoulli keep mask from a Philox
 generator seeded by (seed, offset), and a checker must draw the same mask.
 The page gives no mapping from (seed, offset, element) to Philox words, so
-this oracle fixes one (the reading recorded in the design doc):
+this oracle fixes one (the reading recorded in the design doc).  Each Philox
+block serves four consecutive keys of one row:
 
     key     = (low 32 bits of seed, high 32 bits of seed)
     counter = (low 32 bits of offset, high 32 bits of offset,
-               (i << 16) | j, (b << 16) | h)
-    x       = word 0 of Philox4x32-10(counter, key)
+               (i << 16) | (j - j mod 4), (b << 16) | h)
+    x       = word (j mod 4) of Philox4x32-10(counter, key)
     keep    = x >= T,  T = ceil(p * 2**32)   (exactly x / 2**32 >= p)
 
 The block function is Philox4x32 with 10 rounds as published by Salmon,
@@ -84,7 +85,9 @@ def dropout_uniform_bits(seed, offset, b, h, rows, cols):
     seed = int(seed)
     offset = int(offset)
     key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    w2 = (rows << np.uint64(16)) | cols
+    group = cols & ~np.uint64(3)          # first key of the four that share a block
+    word = (cols & np.uint64(3)).astype(np.int64)
+    w2 = (rows << np.uint64(16)) | group
     w3 = np.uint64((int(b) << 16) | int(h))
     shape = w2.shape
     counter = (
@@ -93,7 +96,9 @@ def dropout_uniform_bits(seed, offset, b, h, rows, cols):
         w2,
         np.full(shape, w3, dtype=np.uint64),
     )
-    return philox4x32_10(counter, key)[0]
+    words = np.stack(philox4x32_10(counter, key))       # [4, rows, cols]
+    word = np.broadcast_to(word, shape)
+    return np.take_along_axis(words, word[None], axis=0)[0]
 
 
 def dropout_keep(seed, offset, b, h, rows, cols, p):

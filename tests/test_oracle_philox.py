@@ -5,7 +5,8 @@ PyTorch's header-only engine (compiled with g++) and rocRAND's (compiled
 with hipcc for the host).  Both are built and run at test time; no output of
 theirs is stored.  Their stream (seed, subsequence, offset) places the seed
 in the key and (offset, subsequence) in the counter words, which is the
-mapping the dropout mask uses with subsequence = (b<<48)|(h<<32)|(i<<16)|j.
+mapping the dropout mask uses with subsequence = (b<<48)|(h<<32)|(i<<16)|j4,
+j4 = j - j mod 4: key j takes word j mod 4 of that block.
 """
 
 import os
@@ -49,8 +50,11 @@ def _cases():
     seeds = [0, 1, 0x5EED, 0xFFFFFFFF, 1 << 32, (1 << 64) - 1]
     seeds += [int(x) for x in rng.integers(0, 2**63, 4)]
     offsets = [0, 1, 0xFFFFFFFF, 1 << 32, (1 << 40) + 12345]
-    coords = [(0, 0, 0, 0), (65535, 65535, 65535, 65535), (1, 2, 3, 4), (3, 15, 8191, 7000)]
+    coords = [(0, 0, 0, 0), (65535, 65535, 65535, 65532), (1, 2, 3, 4), (3, 15, 8191, 7000),
+              (65535, 65535, 65535, 65535), (1, 2, 3, 5)]
     coords += [tuple(int(x) for x in rng.integers(0, 65536, 4)) for _ in range(6)]
+    coords += [tuple(int(x) for x in rng.integers(0, 65536, 3)) + (4 * int(rng.integers(0, 16384)),)
+               for _ in range(6)]
     cases = []
     for s in seeds:
         for o in offsets:
@@ -78,8 +82,11 @@ def test_block_function_matches_witness(witness):
         key = (seed & 0xFFFFFFFF, seed >> 32)
         got = [int(w) for w in oracle.philox4x32_10(counter, key)]
         assert got == words, (seed, off, b, h, i, j)
-        x = oracle.dropout_uniform_bits(seed, off, b, h, [i], [j])[0, 0]
-        assert int(x) == words[0]
+        if j % 4 == 0:
+            # the block of keys j .. j + 3: key j + k draws word k
+            cols = [c for c in range(j, j + 4) if c < 65536]
+            x = oracle.dropout_uniform_bits(seed, off, b, h, [i], cols)[0]
+            assert [int(v) for v in x] == words[:len(cols)], (seed, off, b, h, i, j)
 
 
 def test_keep_threshold_is_exact():
@@ -113,3 +120,15 @@ def test_mask_changes_with_offset_and_head():
     b = oracle.dropout_keep(0x5EED, 1, 0, 0, idx, idx, 0.1)
     c = oracle.dropout_keep(0x5EED, 0, 0, 1, idx, idx, 0.1)
     assert (a != b).mean() > 0.1 and (a != c).mean() > 0.1
+
+
+def test_words_of_one_block_serve_four_keys():
+    """Keys 4m .. 4m + 3 of a row share one block; the next four use the next block."""
+    rows = np.arange(5)
+    cols = np.arange(64)
+    x = oracle.dropout_uniform_bits(0x5EED, 7, 2, 9, rows, cols)
+    for i in rows:
+        for m in range(16):
+            counter = (7, 0, (int(i) << 16) | (4 * m), (2 << 16) | 9)
+            words = [int(w) for w in oracle.philox4x32_10(counter, (0x5EED, 0))]
+            assert [int(v) for v in x[i, 4 * m:4 * m + 4]] == words
