@@ -3,19 +3,18 @@
 // The backward as a KV-outer and a Q-outer pass ("FlashAttention backward",
 // section "The loop structure"):
 //
-//  dkdv_kernel     KV-outer, 4 waves: one workgroup owns 128 keys (32 per
-//                  wave, K and V in registers) of one (b, h) and loops over
-//                  the 64-query blocks that can see them.  For each it
-//                  recomputes S = Q K^T and dP = dO V^T on MFMA, rebuilds
+//  dkdv_q2_kernel  KV-outer (deterministic mode): one workgroup owns 128
+//                  keys of one (b, h) and loops over the 64-query blocks
+//                  that can see them, with 8 waves (two per SIMD): 4 key
+//                  groups x 2 query halves, K and V in LDS.  For each block
+//                  it recomputes S = Q K^T and dP = dO V^T on MFMA, rebuilds
 //                  P = exp(S - L) from the saved LSE ("Lecture 7", "The
 //                  recomputation trick"), forms dS = P * (dP - D) with the
 //                  pre-pass scalar D, and accumulates dV += P~^T dO and
 //                  dK += dS^T Q in fp32 registers, written once at the end.
-//                  In atomic mode it also adds dS K into an fp32 dQ
-//                  accumulator with device atomics.
-//  dkdv_q2_kernel  KV-outer, 8 waves (two per SIMD) for d = 128: the same
-//                  work with K and V in LDS and each query block split
-//                  between two waves per key group.
+//  dkdv_kernel     KV-outer for atomic mode, 4 waves (32 keys each, K and V
+//                  in registers): the same work, plus dS K added into an
+//                  fp32 dQ accumulator with device atomics.
 //  dq_kernel       Q-outer: one workgroup owns 128 queries (32 per wave) and
 //                  streams 32-key blocks through a ring of three LDS
 //                  buffers, recomputing S, P, dP, dS to accumulate dQ = dS K
@@ -52,13 +51,6 @@ struct KvCfg {
   static constexpr int LOADS = BR * CH / NT;
 };
 
-// Workgroups per CU each kernel is compiled for (2 = two waves per SIMD):
-// register budgets of 256 per lane where the kernel fits in them.
-#ifndef KV_MINB_128
-#define KV_MINB_128 1
-#endif
-template <int D, bool ATOMIC>
-constexpr int kv_min_blocks() { return (D == 64 && !ATOMIC) ? 2 : (D == 128 && !ATOMIC ? KV_MINB_128 : 1); }
 
 
 __device__ __forceinline__ bf16x8 load8(const bf16* p) { return *(const bf16x8*)p; }
@@ -92,7 +84,7 @@ __device__ __forceinline__ bool block_dead(const MaskArgs& m, int q0, int nq, in
 // Elementwise step of one 32x32 S/dP accumulator pair of the KV-outer kernel:
 // P = exp2(S * c - L2), masked, dropout, dS = P (dP - D).  Writes the bf16
 // A operands of dV (P~) and dK (dS) for the two 16-query k-steps.
-template <bool GENERAL>
+template <bool GENERAL, bool DROPOK = true>
 __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s, const f32x16& dp,
                                                const float* sLq, const float* sDq, int g, int b,
                                                int h, int q0, int key, bf16x8& pa0, bf16x8& pa1,
@@ -102,7 +94,7 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
   // with e = t (one per rr: bits 4 rr .. 4 rr + 3), and the quad shares them.
   uint32_t kq[4] = {0xFFFFu, 0xFFFFu, 0xFFFFu, 0xFFFFu};
   const int t = key & 3;
-  if (GENERAL && a.m.dropout) {
+  if (GENERAL && DROPOK && a.m.dropout) {
     uint32_t mine = 0;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
@@ -126,7 +118,7 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
         const int qi = q0 + 8 * rr + 4 * g + e;
         p = visible(a.m, qi, key) ? p : 0.f;
         pdrop = p;
-        if (a.m.dropout) {
+        if (DROPOK && a.m.dropout) {
           const bool keep = (kq[e] >> (4 * rr + t)) & 1u;
           pdrop = keep ? p * a.m.keep_scale : 0.f;
           dpv = keep ? dpv * a.m.keep_scale : 0.f;
@@ -150,18 +142,33 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
 // dS = P (dP - D) is formed, then dK += dS^T Q.  qrow/orow point at this
 // lane's query row of the Q and dO tiles (at column 8 g), kr/vr at its key
 // row of K and V; u0 is the first 16-query k-step of the tile.
-template <int D, int LD, typename Mid>
+template <int D, int LD, bool DROP, typename Mid>
 __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow, const bf16* orow,
                                              const bf16* kr, const bf16* vr, const bf16* Qs,
                                              const bf16* Os, const float* sLq, const float* sDq,
                                              int g, int lane, int u0, f32x16* dk_acc,
-                                             f32x16* dv_acc, Mid mid) {
+                                             f32x16* dv_acc, Mid mid, int b, int h, int qs,
+                                             int key) {
   constexpr int KT = D / 16, DT = D / 32;
   const int ulo = 16 * u0 + 4 * g;  // first query row of this lane's k-steps
   f32x16 sacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) sacc = mfma32x32x16(load8(qrow + 16 * t), load8(kr + 16 * t), sacc);
   mid();
+  // dropout keep bits: lane t of a quad draws the blocks of rows e = t and the
+  // quad shares them (keys lie across lanes, four per block)
+  uint32_t kq[4] = {0u, 0u, 0u, 0u};
+  const int kt4 = key & 3;
+  if (DROP) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      mine |= dropout_keep4(a.m, b, h, qs + 8 * rr + 4 * g + kt4, key & ~3) << (4 * rr);
+    kq[0] = __builtin_amdgcn_mov_dpp((int)mine, 0x00, 0xF, 0xF, false);  // quad_perm [0,0,0,0]
+    kq[1] = __builtin_amdgcn_mov_dpp((int)mine, 0x55, 0xF, 0xF, false);  // quad_perm [1,1,1,1]
+    kq[2] = __builtin_amdgcn_mov_dpp((int)mine, 0xAA, 0xF, 0xF, false);  // quad_perm [2,2,2,2]
+    kq[3] = __builtin_amdgcn_mov_dpp((int)mine, 0xFF, 0xF, 0xF, false);  // quad_perm [3,3,3,3]
+  }
   f32x16 dpacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), load8(vr + 16 * t), dpacc);
@@ -177,7 +184,8 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
       p[r] = fast_exp2(sacc[r] * a.scale_log2 - l4[e]);
-      pa[r >> 3][r & 7] = (bf16)p[r];
+      const bool keep = !DROP || ((kq[e] >> (4 * rr + kt4)) & 1u);
+      pa[r >> 3][r & 7] = (bf16)(DROP ? (keep ? p[r] * a.m.keep_scale : 0.f) : p[r]);
     }
   }
 #pragma unroll
@@ -194,7 +202,9 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
-      da[r >> 3][r & 7] = (bf16)(p[r] * (dpacc[r] - d4[e]));
+      float dpv = dpacc[r];
+      if (DROP) dpv = ((kq[e] >> (4 * rr + kt4)) & 1u) ? dpv * a.m.keep_scale : 0.f;
+      da[r >> 3][r & 7] = (bf16)(p[r] * (dpv - d4[e]));
     }
   }
 #pragma unroll
@@ -208,7 +218,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
 // ---------------------------------------------------------------- KV-outer
 
 template <int D, bool ATOMIC>
-__global__ void __launch_bounds__(256, (kv_min_blocks<D, ATOMIC>())) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2][C::BR * C::LD];
   __shared__ __attribute__((aligned(16))) bf16 sO[2][C::BR * C::LD];
@@ -441,7 +451,7 @@ struct KvQCfg {
   static constexpr int KV_LOADS = BC * CH / NT;     // K (and V) chunks per thread, once
 };
 
-template <int D>
+template <int D, bool DROP>
 __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   using C = KvQCfg<D>;
   // [0, 4*BR*LD): Q, dO double buffers; then K and V; reused for the
@@ -531,7 +541,7 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   const bf16* Vr = sV + (32 * grp + c) * C::LD + 8 * g;
   // FULL: every wave's tile fully visible; PRE: the next block exists and is
   // loaded from inside the tile's products
-  auto step = [&](int it, auto full, auto pre) {
+  auto step = [&](int it, auto full, auto pre, auto drop) {
     const int buf = (it - it0) & 1;
     const bool has_next = it + 1 < it1;
     if (!decltype(pre)::value && has_next) load_tile(it + 1);
@@ -539,9 +549,10 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     const bf16* Os = smem + (2 + buf) * TILE;
     const int qs = it * C::BR + 32 * qh;
     if (decltype(full)::value) {
-      kv_full_tile<D, C::LD>(a, Qs + (32 * qh + c) * C::LD + 8 * g, Os + (32 * qh + c) * C::LD + 8 * g, Kr,
-                             Vr, Qs, Os, &sL[buf][32 * qh], &sD[buf][32 * qh], g, lane, 2 * qh, dk_acc,
-                             dv_acc, [&] { if (decltype(pre)::value) load_tile(it + 1); });
+      kv_full_tile<D, C::LD, decltype(drop)::value>(
+          a, Qs + (32 * qh + c) * C::LD + 8 * g, Os + (32 * qh + c) * C::LD + 8 * g, Kr, Vr, Qs, Os,
+          &sL[buf][32 * qh], &sD[buf][32 * qh], g, lane, 2 * qh, dk_acc, dv_acc,
+          [&] { if (decltype(pre)::value) load_tile(it + 1); }, b, h, qs, key);
     } else if (!block_dead(a.m, qs, 32, kvw, 32)) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
@@ -554,7 +565,7 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
       bf16x8 pa0, pa1, da0, da1;
       const float* sLq = &sL[buf][32 * qh];
       const float* sDq = &sD[buf][32 * qh];
-      kv_elementwise<true>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
+      kv_elementwise<true, DROP>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         const int u = 2 * qh + u2;
@@ -575,7 +586,7 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     lds_barrier();
   };
   int itA = it1, itB = it1;
-  if (!a.m.dropout && kv0 + C::BC <= N) {
+  if (kv0 + C::BC <= N) {
     int lo = 0, hi = N - C::BR;
     if (a.m.causal) lo = max(lo, kv0 + C::BC - 1);
     if (a.m.wr >= 0) lo = max(lo, kv0 + C::BC - 1 - a.m.wr);
@@ -587,13 +598,18 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   }
   std::integral_constant<bool, false> general;
   std::integral_constant<bool, true> fast;
-  std::integral_constant<bool, false> no_pre;
-  std::integral_constant<bool, true> pre;
+  std::integral_constant<bool, false> no_pre, no_drop;
+  std::integral_constant<bool, true> pre, drop;
   int it = it0;
-  for (; it < itA; ++it) step(it, general, no_pre);
-  for (; it < min(itB, it1 - 1); ++it) step(it, fast, pre);
-  for (; it < itB; ++it) step(it, fast, no_pre);
-  for (; it < it1; ++it) step(it, general, no_pre);
+  for (; it < itA; ++it) step(it, general, no_pre, no_drop);
+  if (DROP) {
+    for (; it < min(itB, it1 - 1); ++it) step(it, fast, pre, drop);
+    for (; it < itB; ++it) step(it, fast, no_pre, drop);
+  } else {
+    for (; it < min(itB, it1 - 1); ++it) step(it, fast, pre, no_drop);
+    for (; it < itB; ++it) step(it, fast, no_pre, no_drop);
+  }
+  for (; it < it1; ++it) step(it, general, no_pre, no_drop);
 
   // Sum the two query halves of each key group: waves 4..7 hand their
   // partials to waves 0..3 through LDS (value r of tile n of lane l at
@@ -645,7 +661,7 @@ struct QCfg {
   static constexpr int LOADS = BK * CH / NT;
 };
 
-template <int D>
+template <int D, bool DROP>
 __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sK[3][C::BK * C::LD];
@@ -753,7 +769,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   // Key blocks [jtA, jtB) are seen by all 128 queries of the block with no
   // mask edge and no dropout.
   int jtA = jt1, jtB = jt1;
-  if (!a.m.dropout && q0 + C::BQ <= N) {
+  if (q0 + C::BQ <= N) {
     int lo = 0, hi = N - C::BK;
     if (a.m.causal) hi = min(hi, q0 - C::BK + 1);
     if (a.m.wr >= 0) hi = min(hi, q0 + a.m.wr - C::BK + 1);
@@ -776,14 +792,14 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
       for (int rr = 0; rr < 4; ++rr) {
         // keys j4 .. j4 + 3 of this lane's query share one dropout block
         const int j4 = ks + 8 * rr + 4 * g;
-        const uint32_t keep = a.m.dropout ? dropout_keep4(a.m, b, h, myq, j4) : 0xFu;
+        const uint32_t keep = DROP ? dropout_keep4(a.m, b, h, myq, j4) : 0xFu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
           float p = fast_exp2(st[r] * a.scale_log2 - l2);
           float dpv = dpt[r];
           p = visible(a.m, myq, j4 + e) ? p : 0.f;
-          if (a.m.dropout) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
+          if (DROP) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
           const bf16 v = (bf16)(p * (dpv - dd));
           if (r < 8) d0[r] = v; else d1[r - 8] = v;
         }
@@ -795,12 +811,21 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 
   int jt = jt0;
   for (; jt < jtA; ++jt) general(jt);
-  if (jtA < jtB) {
-    auto ds_of = [&](const f32x16& st, const f32x16& dpt, bf16x8& d0, bf16x8& d1) {
+  // the fully visible range, software-pipelined; DROP: with the dropout mask
+  auto fast_range = [&](auto drop) {
+    constexpr bool FDROP = decltype(drop)::value;
+    auto ds_of = [&](int j, const f32x16& st, const f32x16& dpt, bf16x8& d0, bf16x8& d1) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bf16 v = (bf16)(fast_exp2(st[r] * a.scale_log2 - l2) * (dpt[r] - dd));
-        if (r < 8) d0[r] = v; else d1[r - 8] = v;
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint32_t keep = FDROP ? dropout_keep4(a.m, b, h, myq, j * C::BK + 8 * rr + 4 * g) : 0xFu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float dpv = dpt[r];
+          if (FDROP) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
+          const bf16 v = (bf16)(fast_exp2(st[r] * a.scale_log2 - l2) * (dpv - dd));
+          if (r < 8) d0[r] = v; else d1[r - 8] = v;
+        }
       }
     };
     f32x16 st, dpt;
@@ -814,7 +839,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 #pragma unroll
       for (int n = 0; n < C::DT; ++n) b0[n] = tr_operand(Kc, C::LD, 4 * g, 8 + 4 * g, 32 * n, lane);
       bf16x8 d0, d1;
-      ds_of(st, dpt, d0, d1);
+      ds_of(jt, st, dpt, d0, d1);
 #pragma unroll
       for (int n = 0; n < C::DT; ++n) b1[n] = tr_operand(Kc, C::LD, 16 + 4 * g, 24 + 4 * g, 32 * n, lane);
 #pragma unroll
@@ -827,11 +852,12 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
     }
     if (jt + 2 < jt1) load_tile(jt + 2);
     bf16x8 d0, d1;
-    ds_of(st, dpt, d0, d1);
+    ds_of(jt, st, dpt, d0, d1);
     dqmm(ring(jt), d0, d1);
     advance(jt);
     ++jt;
-  }
+  };
+  if (jtA < jtB) fast_range(std::integral_constant<bool, DROP>());
   for (; jt < jt1; ++jt) general(jt);
 
 #pragma unroll
@@ -849,14 +875,13 @@ hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
   const int bh = a.B * a.H;
   const dim3 grid_kv(bh, (a.m.n + KvCfg<D>::BC - 1) / KvCfg<D>::BC);
   if (deterministic) {
-    if (D == 128)
-      hipLaunchKernelGGL((dkdv_q2_kernel<D>), grid_kv, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((dkdv_kernel<D, false>), grid_kv, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(a.m.dropout ? (dkdv_q2_kernel<D, true>) : (dkdv_q2_kernel<D, false>), grid_kv,
+                       dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid_q(bh, (a.m.n + QCfg<D>::BQ - 1) / QCfg<D>::BQ);
-    hipLaunchKernelGGL((dq_kernel<D>), grid_q, dim3(QCfg<D>::NT), 0, s, a);
+    hipLaunchKernelGGL(a.m.dropout ? (dq_kernel<D, true>) : (dq_kernel<D, false>), grid_q, dim3(QCfg<D>::NT),
+                       0, s, a);
   } else {
     hipLaunchKernelGGL((dkdv_kernel<D, true>), grid_kv, dim3(256), 0, s, a);
   }
