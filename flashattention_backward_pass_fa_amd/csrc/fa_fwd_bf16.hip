@@ -39,7 +39,7 @@ __device__ __forceinline__ bf16x8 zero8() {
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, 1) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   using C = FCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][C::BK * C::LD];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][C::BK * C::LD];
