@@ -10,6 +10,8 @@
 // per-row rescale is a per-lane multiply.  Dropout multiplies the weights
 // that feed O but not the normaliser l.
 
+#include <type_traits>
+
 #include "fa_kernels.h"
 
 namespace fa {
@@ -38,7 +40,7 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
-template <int D>
+template <int D, bool DROP>
 __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   using C = FCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][C::BK * C::LD];
@@ -109,7 +111,9 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   }
   __syncthreads();
 
-  for (int jt = jt0; jt < jt1; ++jt) {
+  // One 64-key block.  FULL: every (query, key) of the workgroup's block is
+  // visible, so no element mask is evaluated.
+  auto step = [&](int jt, auto full) {
     const int buf = (jt - jt0) & 1;
     const bool has_next = jt + 1 < jt1;
     if (has_next) load_tile(jt + 1);
@@ -132,9 +136,11 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
         float s2 = st[kt][r] * a.scale_log2;
-        if (!visible(a.m, myq, key)) s2 = -INFINITY;
+        if (!decltype(full)::value) {
+          const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (!visible(a.m, myq, key)) s2 = -INFINITY;
+        }
         st[kt][r] = s2;
         mx = fmaxf(mx, s2);
       }
@@ -142,25 +148,28 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    l_run *= alpha;
+    // rescale only when some lane's running max moved (alpha == 1 otherwise,
+    // and a product with 1 changes nothing)
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+      const float alpha = fast_exp2(m_run - m_use);
+      l_run *= alpha;
 #pragma unroll
-    for (int n = 0; n < C::DT; ++n) oacc[n] *= alpha;
+      for (int n = 0; n < C::DT; ++n) oacc[n] *= alpha;
+    }
     bf16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         // keys j4 .. j4 + 3 of this lane's query share one dropout block
-        const uint32_t keep =
-            a.m.dropout ? dropout_keep4(a.m, b, h, myq, k0 + 32 * kt + 8 * rr + 4 * g) : 0xFu;
+        const uint32_t keep = DROP ? dropout_keep4(a.m, b, h, myq, k0 + 32 * kt + 8 * rr + 4 * g) : 0xFu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
           const float p = fast_exp2(st[kt][r] - m_use);
           l_run += p;
           float pd = p;
-          if (a.m.dropout) pd = (keep >> e) & 1u ? p * a.m.keep_scale : 0.f;
+          if (DROP) pd = (keep >> e) & 1u ? p * a.m.keep_scale : 0.f;
           pb[2 * kt + (r >> 3)][r & 7] = (bf16)pd;
         }
       }
@@ -176,7 +185,27 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     }
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
+  };
+  // Key blocks [jtA, jtB) are seen by all 128 queries of the block with no
+  // mask edge: causality and the right window bound k0 from above, the left
+  // window from below.
+  int jtA = jt1, jtB = jt1;
+  if (q0 + C::BQ <= N) {
+    int lo = 0, hi = N - C::BK;
+    if (a.m.causal) hi = min(hi, q0 - C::BK + 1);
+    if (a.m.wr >= 0) hi = min(hi, q0 + a.m.wr - C::BK + 1);
+    if (a.m.wl >= 0) lo = max(lo, q0 + C::BQ - 1 - a.m.wl);
+    if (lo <= hi) {
+      jtA = min(max(jt0, (lo + C::BK - 1) / C::BK), jt1);
+      jtB = max(jtA, min(jt1, hi / C::BK + 1));
+    }
   }
+  std::integral_constant<bool, false> general;
+  std::integral_constant<bool, true> fast;
+  int jt = jt0;
+  for (; jt < jtA; ++jt) step(jt, general);
+  for (; jt < jtB; ++jt) step(jt, fast);
+  for (; jt < jt1; ++jt) step(jt, general);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (myq < N) {
@@ -200,9 +229,9 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const dim3 grid(a.B * a.H, (a.m.n + 127) / 128);
   if (a.d == 128)
-    hipLaunchKernelGGL(fwd_kernel<128>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(a.m.dropout ? (fwd_kernel<128, true>) : (fwd_kernel<128, false>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(fwd_kernel<64>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(a.m.dropout ? (fwd_kernel<64, true>) : (fwd_kernel<64, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
