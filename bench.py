@@ -179,6 +179,34 @@ def main():
     main_run = measure(args.mode)
     other_mode = "atomic" if args.mode == "deterministic" else "deterministic"
     other_run = measure(other_mode)
+
+    def time_calls(fn, n):
+        """Average ms of n calls of fn on the stream (after one untimed call)."""
+        stream = torch.cuda.current_stream(dev)
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # Forward (fa_fwd) on the same inputs: the pages compare the two passes'
+    # FLOPs (backward ~2.5x) and speed.
+    n_side = max(3, args.steps // 3)
+    fwd_ms = time_calls(lambda: fa.forward(t["q"], t["k"], t["v"], **kw), n_side)
+    # Mask tile skipping: the same backward without the causal mask (its own
+    # forward for O and L), whose time should be ~2x the causal one.
+    nc_ms = None
+    if w.causal:
+        kw_nc = dict(kw, causal=False)
+        o_nc, lse_nc = fa.forward(t["q"], t["k"], t["v"], **kw_nc)
+        nc_ms = time_calls(lambda: fa.backward(t["q"], t["k"], t["v"], o_nc, t["do"], lse_nc,
+                                               deterministic=args.mode == "deterministic", **kw_nc),
+                           n_side)
+        del o_nc, lse_nc
     deterministic = main_run["deterministic"]
     ms_per_step = main_run["ms_per_step"]
     pre_ms, bwd_ms, step_ms = main_run["pre_ms"], main_run["bwd_ms"], main_run["step_ms"]
@@ -227,6 +255,13 @@ def main():
                        "value": round(flops / (other_run["ms_per_step"] * 1e-3) / 1e12, 2)},
         "device": torch.cuda.get_device_name(dev),
     }
+    fwd_flops = flops * 4 / 10  # forward: S and O products, 4 d per visible pair
+    line["forward"] = {"ms": round(fwd_ms, 4), "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+                       "bwd_over_fwd_time": round(ms_per_step / fwd_ms, 3), "bwd_over_fwd_flops": 2.5}
+    if nc_ms is not None:
+        line["causal_skip_check"] = {"noncausal_step_ms": round(nc_ms, 4),
+                                     "causal_over_noncausal_time": round(ms_per_step / nc_ms, 3),
+                                     "visible_fraction": round(flops / credited_flops(w.B, w.H, w.N, w.d), 4)}
     # A plain copy of known size (outside the timed region): profiling runs
     # use its FETCH_SIZE / WRITE_SIZE to calibrate the HBM byte counters.
     src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
