@@ -30,9 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 (= fp16) FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_bwd_bf16.hip",
+KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_bwd16.hip",
                   "flashattention_backward_pass_fa_amd/csrc/fa_device.h"]
 TRAFFIC_FILE = "profiles/fa_bwd_{mode}_train_causal_bf16_traffic.md"
 COPY_CALIBRATION_BYTES = 256 << 20   # one plain device copy, for HBM counter calibration
@@ -115,12 +115,14 @@ def main():
     from flashattention_backward_pass_fa_amd.inputs import WORKLOADS, make_workload_inputs
 
     w = WORKLOADS[args.workload]
-    if w.dtype != "bf16":
-        print("bench.py measures the bf16 workloads", file=sys.stderr)
+    if w.dtype not in ("bf16", "f16"):
+        print("bench.py measures the 16-bit (bf16, fp16) workloads", file=sys.stderr)
         sys.exit(2)
+    tdtype, code = ((torch.bfloat16, fa.FA_DTYPE_BF16) if w.dtype == "bf16"
+                    else (torch.float16, fa.FA_DTYPE_F16))
     dev = torch.device("cuda:0")
     host = make_workload_inputs(w)
-    t = {n: torch.from_numpy(host[n + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    t = {n: torch.from_numpy(host[n + "_bits"].view(np.int16)).view(tdtype).to(dev)
          for n in ("q", "k", "v", "do")}
     kw = dict(sm_scale=w.sm_scale, causal=w.causal, window=(w.window_left, w.window_right),
               dropout_p=w.dropout_p, seed=w.drop_seed, offset=w.drop_offset)
@@ -129,7 +131,7 @@ def main():
     def measure(mode):
         """Time `args.steps` steps of the backward in dQ mode `mode`."""
         deterministic = mode == "deterministic"
-        params = fa.make_params(w.shape, fa.FA_DTYPE_BF16, deterministic=deterministic, **kw)
+        params = fa.make_params(w.shape, code, deterministic=deterministic, **kw)
         ws_bytes = fa.fa_bwd_workspace_bytes(params)
         ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
         ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws_bytes else 0)
@@ -216,12 +218,15 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     achieved = flops / (bwd_avg * 1e-3) / 1e12
-    traffic = measured_traffic(args.mode)
+    # the committed counter summary covers the default workload only
+    traffic = measured_traffic(args.mode) if w.name == "train_causal_bf16" else None
     pre_avg = sum(pre_ms) / len(pre_ms)
     pre_bytes = 2 * w.B * w.H * w.N * w.d * 2 + 4 * w.B * w.H * w.N + ws_bytes
 
     line = {
-        "metric": "attention-backward TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",
+        "metric": ("attention-backward TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
+                   if w.dtype == "bf16" else
+                   "attention-backward TFLOP/s (fp16, causal) and % of MI355X fp16 MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -231,7 +236,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "window": [w.window_left, w.window_right],

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
 ABI_VERSION = 1
 
 STATUS_NAMES = {
@@ -155,6 +156,8 @@ def _dtype_code(t):
     import torch
     if t.dtype == torch.bfloat16:
         return FA_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
     if t.dtype == torch.float32:
         return FA_DTYPE_F32
     raise ValueError(f"unsupported dtype {t.dtype}")

@@ -20,7 +20,17 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_prep.hip", "fa_f32.hip", "fa_fwd_bf16.hip", "fa_bwd_bf16.hip"]
+# (source, extra flags, object name): the 16-bit kernel sources are compiled
+# once for bf16 and once for fp16.
+SOURCES = [
+    ("fa_api.cpp", [], "fa_api"),
+    ("fa_prep.hip", [], "fa_prep"),
+    ("fa_f32.hip", [], "fa_f32"),
+    ("fa_fwd16.hip", [], "fa_fwd16_bf16"),
+    ("fa_bwd16.hip", [], "fa_bwd16_bf16"),
+    ("fa_fwd16.hip", ["-DFA_ELEM_F16"], "fa_fwd16_f16"),
+    ("fa_bwd16.hip", ["-DFA_ELEM_F16"], "fa_bwd16_f16"),
+]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -41,10 +51,11 @@ def hipcc():
     return path
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(entry, verbose):
+    src, extra, name = entry
+    obj = os.path.join(BUILD_DIR, name + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc()] + COMMON_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON_FLAGS + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -23,15 +23,19 @@ thread_local int g_last_hip_error = 0;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// the 16-bit MFMA dtypes
+bool is16(const fa_params* p) { return p->dtype == FA_DTYPE_BF16 || p->dtype == FA_DTYPE_F16; }
+
 fa_status check_params(const fa_params* p) {
   if (!p) return FA_ERR_INVALID_VALUE;
-  if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_BF16) return FA_ERR_NOT_SUPPORTED;
+  if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F16)
+    return FA_ERR_NOT_SUPPORTED;
   if (p->batch < 1 || p->heads < 1 || p->seqlen < 1 || p->head_dim < 1) return FA_ERR_INVALID_VALUE;
   if ((int64_t)p->batch * p->heads > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
   if (p->seqlen > kMaxSeq) return FA_ERR_NOT_SUPPORTED;
   // the kernels number their workgroups (one per head and 64 rows) in an int
   if ((int64_t)p->batch * p->heads * ((p->seqlen + 63) / 64) > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
-  if (p->dtype == FA_DTYPE_BF16 && p->head_dim != 64 && p->head_dim != 128) return FA_ERR_NOT_SUPPORTED;
+  if (is16(p) && p->head_dim != 64 && p->head_dim != 128) return FA_ERR_NOT_SUPPORTED;
   if (p->dtype == FA_DTYPE_F32 && p->head_dim > 128) return FA_ERR_NOT_SUPPORTED;
   if (!std::isfinite(p->sm_scale)) return FA_ERR_INVALID_VALUE;
   if (p->window_left < -1 || p->window_right < -1) return FA_ERR_INVALID_VALUE;
@@ -43,14 +47,14 @@ fa_status check_params(const fa_params* p) {
   return FA_SUCCESS;
 }
 
-// Atomic dQ mode (bf16, deterministic == 0) accumulates dQ in an fp32
-// workspace; every other call has none.
-bool uses_dq_acc(const fa_params* p) { return p->dtype == FA_DTYPE_BF16 && !p->deterministic; }
+// Atomic dQ mode (16-bit dtypes, deterministic == 0) accumulates dQ in an
+// fp32 workspace; every other call has none.
+bool uses_dq_acc(const fa_params* p) { return is16(p) && !p->deterministic; }
 
 fa_status check_tensor(const fa_params* p, const fa_tensor& t) {
   if (!t.ptr) return FA_ERR_INVALID_VALUE;
   if (t.stride_b < 0 || t.stride_h < 0 || t.stride_n < 0) return FA_ERR_INVALID_VALUE;
-  if (p->dtype == FA_DTYPE_BF16) {
+  if (is16(p)) {
     if (!aligned(t.ptr, 16)) return FA_ERR_MISALIGNED;
     if ((t.stride_b % 8) || (t.stride_h % 8) || (t.stride_n % 8)) return FA_ERR_MISALIGNED;
     if (t.stride_n > INT32_MAX) return FA_ERR_NOT_SUPPORTED;  // row offsets are 32-bit products
@@ -160,7 +164,9 @@ fa_status fa_fwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   a.scale_log2 = p->sm_scale * kLog2e;
   a.m = mask_args(p);
   hipStream_t s = (hipStream_t)stream;
-  return launched(p->dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+  if (p->dtype == FA_DTYPE_BF16) return launched(fa::launch_fwd16(a, s));
+  if (p->dtype == FA_DTYPE_F16) return launched(fa::fp16::launch_fwd16(a, s));
+  return launched(fa::launch_fwd_f32(a, s));
 }
 
 size_t fa_bwd_workspace_bytes(const fa_params* p) {
@@ -190,7 +196,7 @@ fa_status fa_bwd_preprocess(const fa_params* p, fa_tensor o, fa_tensor dout, flo
   a.H = p->heads;
   a.N = p->seqlen;
   a.d = p->head_dim;
-  a.bf16 = p->dtype == FA_DTYPE_BF16;
+  a.dtype = p->dtype;
   a.sm_scale = p->sm_scale;
   return launched(fa::launch_preprocess(a, (hipStream_t)stream));
 }
@@ -239,7 +245,8 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   a.m = mask_args(p);
   hipStream_t s = (hipStream_t)stream;
   if (p->dtype == FA_DTYPE_F32) return launched(fa::launch_bwd_f32(a, s));
-  FA_TRY(launched(fa::launch_bwd_bf16(a, !atomic, s)));
+  FA_TRY(launched(p->dtype == FA_DTYPE_F16 ? fa::fp16::launch_bwd16(a, !atomic, s)
+                                             : fa::launch_bwd16(a, !atomic, s)));
   if (atomic) {
     fa::PrepArgs c{};
     c.dq = view(dq);
@@ -248,7 +255,7 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
     c.H = p->heads;
     c.N = p->seqlen;
     c.d = p->head_dim;
-    c.bf16 = 1;
+    c.dtype = p->dtype;
     c.sm_scale = p->sm_scale;
     FA_TRY(launched(fa::launch_dq_convert(c, s)));
   }

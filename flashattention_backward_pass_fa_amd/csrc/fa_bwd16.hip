@@ -1,4 +1,5 @@
-// fa_bwd_bf16.hip - bf16 FlashAttention backward for gfx950 (MFMA 32x32x16).
+// fa_bwd16.hip - 16-bit (bf16 or fp16) FlashAttention backward for gfx950
+// (MFMA 32x32x16).  Compiled once per element type (see fa_device.h).
 //
 // The backward as a KV-outer and a Q-outer pass ("FlashAttention backward",
 // section "The loop structure"):
@@ -20,7 +21,7 @@
 //                  buffers, recomputing S, P, dP, dS to accumulate dQ = dS K
 //                  in registers: the deterministic, atomic-free dQ.
 //
-// Layout in LDS: Q, dO, K, V tiles are row-major bf16 with a padded row
+// Layout in LDS: Q, dO, K, V tiles are row-major 16-bit with a padded row
 // stride.  The k-inside-lane operands of the dV/dK/dQ products are read
 // from those same tiles with ds_read_tr16_b64, so no transposed copies are
 // kept.  Blocks that are fully masked (causal/window) are never visited; a
@@ -34,6 +35,7 @@
 #include "fa_kernels.h"
 
 namespace fa {
+FA_ELEM_NS_BEGIN
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -53,13 +55,13 @@ struct KvCfg {
 
 
 
-__device__ __forceinline__ bf16x8 load8(const bf16* p) { return *(const bf16x8*)p; }
-__device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *(bf16x8*)p = v; }
+__device__ __forceinline__ e16x8 load8(const e16* p) { return *(const e16x8*)p; }
+__device__ __forceinline__ void store8(e16* p, e16x8 v) { *(e16x8*)p = v; }
 
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 z;
+__device__ __forceinline__ e16x8 zero8() {
+  e16x8 z;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+  for (int i = 0; i < 8; ++i) z[i] = (e16)0.0f;
   return z;
 }
 
@@ -82,13 +84,13 @@ __device__ __forceinline__ bool block_dead(const MaskArgs& m, int q0, int nq, in
 }
 
 // Elementwise step of one 32x32 S/dP accumulator pair of the KV-outer kernel:
-// P = exp2(S * c - L2), masked, dropout, dS = P (dP - D).  Writes the bf16
+// P = exp2(S * c - L2), masked, dropout, dS = P (dP - D).  Writes the 16-bit
 // A operands of dV (P~) and dK (dS) for the two 16-query k-steps.
 template <bool GENERAL, bool DROPOK = true>
 __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s, const f32x16& dp,
                                                const float* sLq, const float* sDq, int g, int b,
-                                               int h, int q0, int key, bf16x8& pa0, bf16x8& pa1,
-                                               bf16x8& da0, bf16x8& da1) {
+                                               int h, int q0, int key, e16x8& pa0, e16x8& pa1,
+                                               e16x8& da0, e16x8& da1) {
   // Dropout: keys across lanes, so the four lanes of a quad hold the four keys
   // of one Philox block.  Lane t of the quad draws the blocks of the rows
   // with e = t (one per rr: bits 4 rr .. 4 rr + 3), and the quad shares them.
@@ -126,11 +128,11 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
       }
       const float ds = p * (dpv - d4[e]);
       if (r < 8) {
-        pa0[r] = (bf16)pdrop;
-        da0[r] = (bf16)ds;
+        pa0[r] = (e16)pdrop;
+        da0[r] = (e16)ds;
       } else {
-        pa1[r - 8] = (bf16)pdrop;
-        da1[r - 8] = (bf16)ds;
+        pa1[r - 8] = (e16)pdrop;
+        da1[r - 8] = (e16)ds;
       }
     }
   }
@@ -143,9 +145,9 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
 // lane's query row of the Q and dO tiles (at column 8 g), kr/vr at its key
 // row of K and V; u0 is the first 16-query k-step of the tile.
 template <int D, int LD, bool DROP, typename Mid>
-__device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow, const bf16* orow,
-                                             const bf16* kr, const bf16* vr, const bf16* Qs,
-                                             const bf16* Os, const float* sLq, const float* sDq,
+__device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, const e16* orow,
+                                             const e16* kr, const e16* vr, const e16* Qs,
+                                             const e16* Os, const float* sLq, const float* sDq,
                                              int g, int lane, int u0, f32x16* dk_acc,
                                              f32x16* dv_acc, Mid mid, int b, int h, int qs,
                                              int key) {
@@ -172,11 +174,11 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
   f32x16 dpacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), load8(vr + 16 * t), dpacc);
-  bf16x8 b0[DT], b1[DT];
+  e16x8 b0[DT], b1[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) b0[n] = tr_operand(Os, LD, ulo, ulo + 8, 32 * n, lane);
   float p[16];
-  bf16x8 pa[2], da[2];
+  e16x8 pa[2], da[2];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
@@ -185,7 +187,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
       const int r = 4 * rr + e;
       p[r] = fast_exp2(sacc[r] * a.scale_log2 - l4[e]);
       const bool keep = !DROP || ((kq[e] >> (4 * rr + kt4)) & 1u);
-      pa[r >> 3][r & 7] = (bf16)(DROP ? (keep ? p[r] * a.m.keep_scale : 0.f) : p[r]);
+      pa[r >> 3][r & 7] = (e16)(DROP ? (keep ? p[r] * a.m.keep_scale : 0.f) : p[r]);
     }
   }
 #pragma unroll
@@ -204,7 +206,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
       const int r = 4 * rr + e;
       float dpv = dpacc[r];
       if (DROP) dpv = ((kq[e] >> (4 * rr + kt4)) & 1u) ? dpv * a.m.keep_scale : 0.f;
-      da[r >> 3][r & 7] = (bf16)(p[r] * (dpv - d4[e]));
+      da[r >> 3][r & 7] = (e16)(p[r] * (dpv - d4[e]));
     }
   }
 #pragma unroll
@@ -220,10 +222,10 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const bf16* qrow,
 template <int D, bool ATOMIC>
 __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   using C = KvCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][C::BR * C::LD];
-  __shared__ __attribute__((aligned(16))) bf16 sO[2][C::BR * C::LD];
-  __shared__ __attribute__((aligned(16))) bf16 sK[ATOMIC ? C::BC * C::LD : 8];
-  __shared__ __attribute__((aligned(16))) bf16 sT[ATOMIC ? C::BC * C::LDS_T : 8];
+  __shared__ __attribute__((aligned(16))) e16 sQ[2][C::BR * C::LD];
+  __shared__ __attribute__((aligned(16))) e16 sO[2][C::BR * C::LD];
+  __shared__ __attribute__((aligned(16))) e16 sK[ATOMIC ? C::BC * C::LD : 8];
+  __shared__ __attribute__((aligned(16))) e16 sT[ATOMIC ? C::BC * C::LDS_T : 8];
   __shared__ __attribute__((aligned(16))) float sL[2][C::BR];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BR];
 
@@ -245,11 +247,11 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   const int it1 = q_lo < q_hi ? (q_hi + C::BR - 1) / C::BR : it0;
 
   // This wave's 32 keys: B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kreg[C::KT], vreg[C::KT];
+  e16x8 kreg[C::KT], vreg[C::KT];
   {
     const bool ok = key < N;
-    const bf16* kp = at<bf16>(a.k, b, h, ok ? key : 0);
-    const bf16* vp = at<bf16>(a.v, b, h, ok ? key : 0);
+    const e16* kp = at<e16>(a.k, b, h, ok ? key : 0);
+    const e16* vp = at<e16>(a.v, b, h, ok ? key : 0);
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) {
       kreg[t] = ok ? load8(kp + 16 * t + 8 * g) : zero8();
@@ -262,12 +264,12 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int kr = kv0 + row;
-      store8(sK + row * C::LD + col, kr < N ? load8(at<bf16>(a.k, b, h, kr) + col) : zero8());
+      store8(sK + row * C::LD + col, kr < N ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
     }
   }
 
   const int64_t row_base = (int64_t)bh * N;
-  bf16x8 pq[C::LOADS], po[C::LOADS];
+  e16x8 pq[C::LOADS], po[C::LOADS];
   float pl = 0.f, pd = 0.f;
 
   auto load_tile = [&](int it) {
@@ -278,8 +280,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int qr = q0 + row;
       if (qr < N) {
-        pq[x] = load8(at<bf16>(a.q, b, h, qr) + col);
-        po[x] = load8(at<bf16>(a.dout, b, h, qr) + col);
+        pq[x] = load8(at<e16>(a.q, b, h, qr) + col);
+        po[x] = load8(at<e16>(a.dout, b, h, qr) + col);
       } else {
         pq[x] = zero8();
         po[x] = zero8();
@@ -322,17 +324,17 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
     const int buf = (it - it0) & 1;
     const bool has_next = it + 1 < it1;
     if (has_next) load_tile(it + 1);
-    const bf16* Qs = sQ[buf];
-    const bf16* Os = sO[buf];
+    const e16* Qs = sQ[buf];
+    const e16* Os = sO[buf];
     const int q0 = it * C::BR;
 
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int qs = q0 + 32 * qt;  // first query of this 32-query sub-tile
-      bf16x8 pa0, pa1, da0, da1;
+      e16x8 pa0, pa1, da0, da1;
       if (!block_dead(a.m, qs, 32, kvw, 32)) {
         // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-        bf16x8 aq[C::KT], ao[C::KT];
+        e16x8 aq[C::KT], ao[C::KT];
 #pragma unroll
         for (int t = 0; t < C::KT; ++t) {
           aq[t] = load8(Qs + (32 * qt + c) * C::LD + 16 * t + 8 * g);
@@ -355,7 +357,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int u2 = 0; u2 < 2; ++u2) {
           const int u = 2 * qt + u2;
-          bf16x8 bo[C::DT], bq[C::DT];
+          e16x8 bo[C::DT], bq[C::DT];
 #pragma unroll
           for (int n = 0; n < C::DT; ++n) {
             bo[n] = tr_operand(Os, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
@@ -375,10 +377,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
         // dS^T of this wave's keys into LDS: sT[key][query]
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const bf16x8 src = rr < 2 ? da0 : da1;
+          const e16x8 src = rr < 2 ? da0 : da1;
           const int s0 = (rr & 1) * 4;
-          const bf16x4 v4 = {src[s0], src[s0 + 1], src[s0 + 2], src[s0 + 3]};
-          *(bf16x4*)(sT + (32 * w + c) * C::LDS_T + 32 * qt + 8 * rr + 4 * g) = v4;
+          const e16x4 v4 = {src[s0], src[s0 + 1], src[s0 + 2], src[s0 + 3]};
+          *(e16x4*)(sT + (32 * w + c) * C::LDS_T + 32 * qt + 8 * rr + 4 * g) = v4;
         }
       }
     }
@@ -394,10 +396,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
       for (int mi = 0; mi < MT; ++mi) dq[mi] = f32x16{};
 #pragma unroll
       for (int t = 0; t < C::BC / 16; ++t) {
-        const bf16x8 bk = tr_operand(sK, C::LD, 16 * t + 8 * g, 16 * t + 8 * g + 4, 32 * nt, lane);
+        const e16x8 bk = tr_operand(sK, C::LD, 16 * t + 8 * g, 16 * t + 8 * g + 4, 32 * nt, lane);
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-          const bf16x8 as =
+          const e16x8 as =
               tr_operand(sT, C::LDS_T, 16 * t + 8 * g, 16 * t + 8 * g + 4, 32 * (mt0 + mi), lane);
           dq[mi] = mfma32x32x16(as, bk, dq[mi]);
         }
@@ -419,15 +421,15 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
     lds_barrier();
   }
 
-  // dK = sm_scale * dS^T Q, dV = P~^T dO: one rounding to bf16 at the store.
+  // dK = sm_scale * dS^T Q, dV = P~^T dO: one rounding to the element type at the store.
 #pragma unroll
   for (int n = 0; n < C::DT; ++n) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (kr < N) {
-        at<bf16>(a.dk, b, h, kr)[32 * n + c] = (bf16)(dk_acc[n][r] * a.sm_scale);
-        at<bf16>(a.dv, b, h, kr)[32 * n + c] = (bf16)(dv_acc[n][r]);
+        at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dk_acc[n][r] * a.sm_scale);
+        at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dv_acc[n][r]);
       }
     }
   }
@@ -457,12 +459,12 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   // [0, 4*BR*LD): Q, dO double buffers; then K and V; reused for the
   // partial-sum exchange after the loop.
   constexpr int TILE = C::BR * C::LD, KVT = C::BC * C::LD;
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE + 2 * KVT];
+  __shared__ __attribute__((aligned(16))) e16 smem[4 * TILE + 2 * KVT];
   __shared__ __attribute__((aligned(16))) float sL[2][C::BR];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BR];
   // Q buffers at smem + buf * TILE, dO buffers at smem + (2 + buf) * TILE
-  bf16* sK = smem + 4 * TILE;
-  bf16* sV = sK + KVT;
+  e16* sK = smem + 4 * TILE;
+  e16* sV = sK + KVT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
@@ -487,15 +489,15 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     const int chunk = tid + x * C::NT;
     const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
     const int kr = kv0 + row;
-    store8(sK + row * C::LD + col, kr < N ? load8(at<bf16>(a.k, b, h, kr) + col) : zero8());
-    store8(sV + row * C::LD + col, kr < N ? load8(at<bf16>(a.v, b, h, kr) + col) : zero8());
+    store8(sK + row * C::LD + col, kr < N ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
+    store8(sV + row * C::LD + col, kr < N ? load8(at<e16>(a.v, b, h, kr) + col) : zero8());
   }
 
   const int64_t row_base = (int64_t)bh * N;
-  const char* q_head = (const char*)at<bf16>(a.q, b, h, 0);
-  const char* o_head = (const char*)at<bf16>(a.dout, b, h, 0);
+  const char* q_head = (const char*)at<e16>(a.q, b, h, 0);
+  const char* o_head = (const char*)at<e16>(a.dout, b, h, 0);
   const uint32_t q_rs = (uint32_t)a.q.sn * 2, o_rs = (uint32_t)a.dout.sn * 2;
-  bf16x8 pq[C::LOADS], po[C::LOADS];
+  e16x8 pq[C::LOADS], po[C::LOADS];
   float pld = 0.f;
   auto load_tile = [&](int it) {
     const int q0 = it * C::BR;
@@ -504,8 +506,8 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int qr = min(q0 + row, N - 1);
-      pq[x] = load8((const bf16*)row_addr(q_head, q_rs, qr) + col);
-      po[x] = load8((const bf16*)row_addr(o_head, o_rs, qr) + col);
+      pq[x] = load8((const e16*)row_addr(q_head, q_rs, qr) + col);
+      po[x] = load8((const e16*)row_addr(o_head, o_rs, qr) + col);
     }
     if (tid < 2 * C::BR) {
       const int qr = q0 + (tid & (C::BR - 1));
@@ -537,16 +539,16 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  const bf16* Kr = sK + (32 * grp + c) * C::LD + 8 * g;  // this lane's key row (B operands)
-  const bf16* Vr = sV + (32 * grp + c) * C::LD + 8 * g;
+  const e16* Kr = sK + (32 * grp + c) * C::LD + 8 * g;  // this lane's key row (B operands)
+  const e16* Vr = sV + (32 * grp + c) * C::LD + 8 * g;
   // FULL: every wave's tile fully visible; PRE: the next block exists and is
   // loaded from inside the tile's products
   auto step = [&](int it, auto full, auto pre, auto drop) {
     const int buf = (it - it0) & 1;
     const bool has_next = it + 1 < it1;
     if (!decltype(pre)::value && has_next) load_tile(it + 1);
-    const bf16* Qs = smem + buf * TILE;
-    const bf16* Os = smem + (2 + buf) * TILE;
+    const e16* Qs = smem + buf * TILE;
+    const e16* Os = smem + (2 + buf) * TILE;
     const int qs = it * C::BR + 32 * qh;
     if (decltype(full)::value) {
       kv_full_tile<D, C::LD, decltype(drop)::value>(
@@ -557,19 +559,19 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int t = 0; t < C::KT; ++t) {
-        const bf16x8 aq = load8(Qs + (32 * qh + c) * C::LD + 16 * t + 8 * g);
-        const bf16x8 ao = load8(Os + (32 * qh + c) * C::LD + 16 * t + 8 * g);
+        const e16x8 aq = load8(Qs + (32 * qh + c) * C::LD + 16 * t + 8 * g);
+        const e16x8 ao = load8(Os + (32 * qh + c) * C::LD + 16 * t + 8 * g);
         sacc = mfma32x32x16(aq, load8(Kr + 16 * t), sacc);
         dpacc = mfma32x32x16(ao, load8(Vr + 16 * t), dpacc);
       }
-      bf16x8 pa0, pa1, da0, da1;
+      e16x8 pa0, pa1, da0, da1;
       const float* sLq = &sL[buf][32 * qh];
       const float* sDq = &sD[buf][32 * qh];
       kv_elementwise<true, DROP>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         const int u = 2 * qh + u2;
-        bf16x8 bo[C::DT], bq[C::DT];
+        e16x8 bo[C::DT], bq[C::DT];
 #pragma unroll
         for (int n = 0; n < C::DT; ++n) {
           bo[n] = tr_operand(Os, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
@@ -634,8 +636,8 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
         const float dvv = dv_acc[n][r] + xch[((grp * 2 * C::DT + C::DT + n) * 16 + r) * 64 + lane];
         const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
         if (kr < N) {
-          at<bf16>(a.dk, b, h, kr)[32 * n + c] = (bf16)(dkv * a.sm_scale);
-          at<bf16>(a.dv, b, h, kr)[32 * n + c] = (bf16)(dvv);
+          at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dkv * a.sm_scale);
+          at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dvv);
         }
       }
     }
@@ -664,8 +666,8 @@ struct QCfg {
 template <int D, bool DROP>
 __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sK[3][C::BK * C::LD];
-  __shared__ __attribute__((aligned(16))) bf16 sV[3][C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) e16 sK[3][C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) e16 sV[3][C::BK * C::LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
@@ -680,11 +682,11 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   const int64_t row_base = (int64_t)bh * N;
 
   // This wave's 32 queries: B operands of S^T = K Q^T and dP^T = V dO^T.
-  bf16x8 qreg[C::KT], oreg[C::KT];
+  e16x8 qreg[C::KT], oreg[C::KT];
   {
     const bool ok = myq < N;
-    const bf16* qp = at<bf16>(a.q, b, h, ok ? myq : 0);
-    const bf16* op = at<bf16>(a.dout, b, h, ok ? myq : 0);
+    const e16* qp = at<e16>(a.q, b, h, ok ? myq : 0);
+    const e16* op = at<e16>(a.dout, b, h, ok ? myq : 0);
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) {
       qreg[t] = ok ? load8(qp + 16 * t + 8 * g) : zero8();
@@ -701,10 +703,10 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   const int jt0 = k_lo / C::BK;
   const int jt1 = k_lo < k_hi ? (k_hi + C::BK - 1) / C::BK : jt0;
 
-  const char* k_head = (const char*)at<bf16>(a.k, b, h, 0);
-  const char* v_head = (const char*)at<bf16>(a.v, b, h, 0);
+  const char* k_head = (const char*)at<e16>(a.k, b, h, 0);
+  const char* v_head = (const char*)at<e16>(a.v, b, h, 0);
   const uint32_t k_rs = (uint32_t)a.k.sn * 2, v_rs = (uint32_t)a.v.sn * 2;
-  bf16x8 pk[C::LOADS], pv[C::LOADS];
+  e16x8 pk[C::LOADS], pv[C::LOADS];
   auto load_tile = [&](int jt) {
     const int k0 = jt * C::BK;
 #pragma unroll
@@ -712,8 +714,8 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int kr = min(k0 + row, N - 1);  // rows past the end are masked: read a valid one
-      pk[x] = load8((const bf16*)row_addr(k_head, k_rs, kr) + col);
-      pv[x] = load8((const bf16*)row_addr(v_head, v_rs, kr) + col);
+      pk[x] = load8((const e16*)row_addr(k_head, k_rs, kr) + col);
+      pv[x] = load8((const e16*)row_addr(v_head, v_rs, kr) + col);
     }
   };
   auto store_tile = [&](int buf) {
@@ -741,7 +743,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
       dpt = mfma32x32x16(load8(&sV[buf][c * C::LD + 16 * t + 8 * g]), oreg[t], dpt);
     }
   };
-  auto dqmm = [&](int buf, const bf16x8& d0, const bf16x8& d1) {
+  auto dqmm = [&](int buf, const e16x8& d0, const e16x8& d1) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -787,7 +789,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
     if (!block_dead(a.m, qw, 32, ks, 32)) {
       f32x16 st, dpt;
       sdp(buf, st, dpt);
-      bf16x8 d0, d1;
+      e16x8 d0, d1;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         // keys j4 .. j4 + 3 of this lane's query share one dropout block
@@ -800,7 +802,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
           float dpv = dpt[r];
           p = visible(a.m, myq, j4 + e) ? p : 0.f;
           if (DROP) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
-          const bf16 v = (bf16)(p * (dpv - dd));
+          const e16 v = (e16)(p * (dpv - dd));
           if (r < 8) d0[r] = v; else d1[r - 8] = v;
         }
       }
@@ -814,7 +816,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   // the fully visible range, software-pipelined; DROP: with the dropout mask
   auto fast_range = [&](auto drop) {
     constexpr bool FDROP = decltype(drop)::value;
-    auto ds_of = [&](int j, const f32x16& st, const f32x16& dpt, bf16x8& d0, bf16x8& d1) {
+    auto ds_of = [&](int j, const f32x16& st, const f32x16& dpt, e16x8& d0, e16x8& d1) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const uint32_t keep = FDROP ? dropout_keep4(a.m, b, h, myq, j * C::BK + 8 * rr + 4 * g) : 0xFu;
@@ -823,7 +825,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
           const int r = 4 * rr + e;
           float dpv = dpt[r];
           if (FDROP) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
-          const bf16 v = (bf16)(fast_exp2(st[r] * a.scale_log2 - l2) * (dpv - dd));
+          const e16 v = (e16)(fast_exp2(st[r] * a.scale_log2 - l2) * (dpv - dd));
           if (r < 8) d0[r] = v; else d1[r - 8] = v;
         }
       }
@@ -834,11 +836,11 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
       if (jt + 2 < jt1) load_tile(jt + 2);
       f32x16 st_n, dpt_n;
       sdp(ring(jt + 1), st_n, dpt_n);
-      const bf16* Kc = sK[ring(jt)];
-      bf16x8 b0[C::DT], b1[C::DT];
+      const e16* Kc = sK[ring(jt)];
+      e16x8 b0[C::DT], b1[C::DT];
 #pragma unroll
       for (int n = 0; n < C::DT; ++n) b0[n] = tr_operand(Kc, C::LD, 4 * g, 8 + 4 * g, 32 * n, lane);
-      bf16x8 d0, d1;
+      e16x8 d0, d1;
       ds_of(jt, st, dpt, d0, d1);
 #pragma unroll
       for (int n = 0; n < C::DT; ++n) b1[n] = tr_operand(Kc, C::LD, 16 + 4 * g, 24 + 4 * g, 32 * n, lane);
@@ -851,7 +853,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
       dpt = dpt_n;
     }
     if (jt + 2 < jt1) load_tile(jt + 2);
-    bf16x8 d0, d1;
+    e16x8 d0, d1;
     ds_of(jt, st, dpt, d0, d1);
     dqmm(ring(jt), d0, d1);
     advance(jt);
@@ -865,7 +867,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qr = qw + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (qr < N) at<bf16>(a.dq, b, h, qr)[32 * n + c] = (bf16)(dq_acc[n][r] * a.sm_scale);
+      if (qr < N) at<e16>(a.dq, b, h, qr)[32 * n + c] = (e16)(dq_acc[n][r] * a.sm_scale);
     }
   }
 }
@@ -890,8 +892,9 @@ hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, bool deterministic, hipStream_t s) {
+hipError_t launch_bwd16(const BwdArgs& a, bool deterministic, hipStream_t s) {
   return a.d == 128 ? launch_d<128>(a, deterministic, s) : launch_d<64>(a, deterministic, s);
 }
 
+FA_ELEM_NS_END
 }  // namespace fa

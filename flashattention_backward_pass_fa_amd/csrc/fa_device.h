@@ -28,6 +28,26 @@ namespace fa {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Element type of the 16-bit MFMA kernels.  Their sources (fa_fwd16.hip,
+// fa_bwd16.hip) are compiled twice: for bf16, and with FA_ELEM_F16 for fp16,
+// whose kernels and launchers live in namespace fa::fp16.
+#ifdef FA_ELEM_F16
+typedef f16 e16;
+typedef f16x8 e16x8;
+typedef f16x4 e16x4;
+#define FA_ELEM_NS_BEGIN namespace fp16 {
+#define FA_ELEM_NS_END }
+#else
+typedef bf16 e16;
+typedef bf16x8 e16x8;
+typedef bf16x4 e16x4;
+#define FA_ELEM_NS_BEGIN
+#define FA_ELEM_NS_END
+#endif
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -57,34 +77,37 @@ struct MaskArgs {
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// 8 bytes (4 bf16) transposed out of LDS, see the header comment.
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+// 8 bytes (4 16-bit elements) transposed out of LDS, see the header comment.
+__device__ __forceinline__ e16x4 lds_read_tr(const e16* p) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
+  return __builtin_bit_cast(e16x4, v);
 }
 
-__device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ e16x8 concat(e16x4 lo, e16x4 hi) {
+  return e16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// k-inside-lane operand for one 32x32x16 step from a row-major bf16 tile
+// k-inside-lane operand for one 32x32x16 step from a row-major 16-bit tile
 // (row stride ld elements): lane l gets rows row_lo + (0..3) and
 // row_hi + (0..3) of column col0 + l % 32, where row_lo/row_hi already
 // include the lane half's offset.  Every lane passes its own row bases.
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ld, int row_lo, int row_hi,
-                                             int col0, int lane) {
+__device__ __forceinline__ e16x8 tr_operand(const e16* tile, int ld, int row_lo, int row_hi,
+                                            int col0, int lane) {
   const int j = lane & 15;
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-  const bf16x4 lo = lds_read_tr(tile + (row_lo + (j >> 2)) * ld + col);
-  const bf16x4 hi = lds_read_tr(tile + (row_hi + (j >> 2)) * ld + col);
+  const e16x4 lo = lds_read_tr(tile + (row_lo + (j >> 2)) * ld + col);
+  const e16x4 hi = lds_read_tr(tile + (row_hi + (j >> 2)) * ld + col);
   return concat(lo, hi);
 }
 
-// Row stride (bf16 elements) of a row-major LDS tile of `cols` columns.
+// Row stride (16-bit elements) of a row-major LDS tile of `cols` columns.
 // Measured on gfx950 (64 banks of 4 bytes): a b128 row read by 16 lanes of
 // consecutive rows is conflict-free when the stride in dwords is an odd
 // multiple of 4 modulo 64, and the transposed 8-byte read, which touches 4

@@ -1,4 +1,5 @@
-// fa_fwd_bf16.hip - bf16 FlashAttention forward for gfx950, emitting O and L.
+// fa_fwd16.hip - 16-bit (bf16 or fp16) FlashAttention forward for gfx950,
+// emitting O and L.  Compiled once per element type (see fa_device.h).
 //
 // "FlashAttention backward", section "What the forward left behind": the
 // forward keeps only O and the per-row log-sum-exp L_i = m_i + log l_i.
@@ -15,6 +16,7 @@
 #include "fa_kernels.h"
 
 namespace fa {
+FA_ELEM_NS_BEGIN
 namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
@@ -31,20 +33,20 @@ struct FCfg {
   static constexpr int LOADS = BK * CH / NT;
 };
 
-__device__ __forceinline__ bf16x8 load8(const bf16* p) { return *(const bf16x8*)p; }
-__device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *(bf16x8*)p = v; }
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 z;
+__device__ __forceinline__ e16x8 load8(const e16* p) { return *(const e16x8*)p; }
+__device__ __forceinline__ void store8(e16* p, e16x8 v) { *(e16x8*)p = v; }
+__device__ __forceinline__ e16x8 zero8() {
+  e16x8 z;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+  for (int i = 0; i < 8; ++i) z[i] = (e16)0.0f;
   return z;
 }
 
 template <int D, bool DROP>
 __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   using C = FCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][C::BK * C::LD];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) e16 sK[2][C::BK * C::LD];
+  __shared__ __attribute__((aligned(16))) e16 sV[2][C::BK * C::LD];
 
   const int tid = threadIdx.x;
   // the wave index is uniform across the wave: keep it (and all derived from it) scalar
@@ -57,10 +59,10 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
 
-  bf16x8 qreg[C::KT];
+  e16x8 qreg[C::KT];
   {
     const bool ok = myq < N;
-    const bf16* qp = at<bf16>(a.q, b, h, ok ? myq : 0);
+    const e16* qp = at<e16>(a.q, b, h, ok ? myq : 0);
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) qreg[t] = ok ? load8(qp + 16 * t + 8 * g) : zero8();
   }
@@ -72,7 +74,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const int jt0 = k_lo / C::BK;
   const int jt1 = k_lo < k_hi ? (k_hi + C::BK - 1) / C::BK : jt0;
 
-  bf16x8 pk[C::LOADS], pv[C::LOADS];
+  e16x8 pk[C::LOADS], pv[C::LOADS];
   auto load_tile = [&](int jt) {
     const int k0 = jt * C::BK;
 #pragma unroll
@@ -81,8 +83,8 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int kr = k0 + row;
       if (kr < N) {
-        pk[x] = load8(at<bf16>(a.k, b, h, kr) + col);
-        pv[x] = load8(at<bf16>(a.v, b, h, kr) + col);
+        pk[x] = load8(at<e16>(a.k, b, h, kr) + col);
+        pv[x] = load8(at<e16>(a.v, b, h, kr) + col);
       } else {
         pk[x] = zero8();
         pv[x] = zero8();
@@ -117,8 +119,8 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     const int buf = (jt - jt0) & 1;
     const bool has_next = jt + 1 < jt1;
     if (has_next) load_tile(jt + 1);
-    const bf16* Ks = sK[buf];
-    const bf16* Vs = sV[buf];
+    const e16* Ks = sK[buf];
+    const e16* Vs = sV[buf];
     const int k0 = jt * C::BK;
 
     f32x16 st[2];
@@ -127,7 +129,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
       st[kt] = f32x16{};
 #pragma unroll
       for (int t = 0; t < C::KT; ++t) {
-        const bf16x8 ak = load8(Ks + (32 * kt + c) * C::LD + 16 * t + 8 * g);
+        const e16x8 ak = load8(Ks + (32 * kt + c) * C::LD + 16 * t + 8 * g);
         st[kt] = mfma32x32x16(ak, qreg[t], st[kt]);
       }
     }
@@ -156,7 +158,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int n = 0; n < C::DT; ++n) oacc[n] *= alpha;
     }
-    bf16x8 pb[4];
+    e16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -170,7 +172,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
           l_run += p;
           float pd = p;
           if (DROP) pd = (keep >> e) & 1u ? p * a.m.keep_scale : 0.f;
-          pb[2 * kt + (r >> 3)][r & 7] = (bf16)pd;
+          pb[2 * kt + (r >> 3)][r & 7] = (e16)pd;
         }
       }
     }
@@ -179,7 +181,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     for (int n = 0; n < C::DT; ++n) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 av = tr_operand(Vs, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
+        const e16x8 av = tr_operand(Vs, C::LD, 16 * u + 4 * g, 16 * u + 8 + 4 * g, 32 * n, lane);
         oacc[n] = mfma32x32x16(av, pb[u], oacc[n]);
       }
     }
@@ -210,14 +212,14 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (myq < N) {
     const float inv = 1.0f / l_tot;
-    bf16* op = at<bf16>(a.o, b, h, myq);
+    e16* op = at<e16>(a.o, b, h, myq);
 #pragma unroll
     for (int n = 0; n < C::DT; ++n) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const bf16x4 v4 = {(bf16)(oacc[n][4 * rr] * inv), (bf16)(oacc[n][4 * rr + 1] * inv),
-                           (bf16)(oacc[n][4 * rr + 2] * inv), (bf16)(oacc[n][4 * rr + 3] * inv)};
-        *(bf16x4*)(op + 32 * n + 8 * rr + 4 * g) = v4;
+        const e16x4 v4 = {(e16)(oacc[n][4 * rr] * inv), (e16)(oacc[n][4 * rr + 1] * inv),
+                           (e16)(oacc[n][4 * rr + 2] * inv), (e16)(oacc[n][4 * rr + 3] * inv)};
+        *(e16x4*)(op + 32 * n + 8 * rr + 4 * g) = v4;
       }
     }
     if (g == 0) a.lse[(int64_t)bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
@@ -226,7 +228,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
   const dim3 grid(a.B * a.H, (a.m.n + 127) / 128);
   if (a.d == 128)
     hipLaunchKernelGGL(a.m.dropout ? (fwd_kernel<128, true>) : (fwd_kernel<128, false>), grid, dim3(256), 0, s, a);
@@ -235,4 +237,5 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+FA_ELEM_NS_END
 }  // namespace fa

@@ -36,16 +36,20 @@ struct PrepArgs {
   float* delta;
   float* dq_acc;
   int B, H, N, d;
-  int bf16;            // element type of o/dout/dq
+  int dtype;           // element type of o/dout/dq: 0 fp32, 1 bf16, 2 fp16 (fa_dtype)
   float sm_scale;
 };
 
 // Launchers: return hipSuccess or the launch error.  No validation here;
 // the C-ABI layer validates every argument first.
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);  // bf16 (fp16: in namespace fp16)
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs& a, bool deterministic, hipStream_t s);
+hipError_t launch_bwd16(const BwdArgs& a, bool deterministic, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
+namespace fp16 {
+hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd16(const BwdArgs& a, bool deterministic, hipStream_t s);
+}  // namespace fp16
 hipError_t launch_preprocess(const PrepArgs& a, hipStream_t s);
 hipError_t launch_dq_convert(const PrepArgs& a, hipStream_t s);
 hipError_t launch_dropout_mask(const MaskArgs& m, int b, int h, uint8_t* out, hipStream_t s);

@@ -5,7 +5,7 @@
 //                     the one scalar that makes them local": one cheap pass
 //                     over dO and O before the main loop), fused with zeroing
 //                     the fp32 dQ accumulator of atomic mode.
-//  dq_convert_kernel  dQ = round_bf16(sm_scale * dQ_acc).
+//  dq_convert_kernel  dQ = round_to_dtype(sm_scale * dQ_acc) (bf16 or fp16).
 //  mask_kernel        the dropout keep mask of one head (test aid).
 //
 // prep_kernel: 16 lanes per row, each lane loads 16 contiguous bytes of O
@@ -20,6 +20,33 @@ namespace {
 
 constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per row
 
+// this lane's share of sum_k dO_k O_k over a 16-bit row (8 elements per step)
+template <typename T, typename T8>
+__device__ __forceinline__ float row_dot16(const TensorView& o, const TensorView& g, int b, int h, int n,
+                                           int d, int sub) {
+  const T* op = at<T>(o, b, h, n);
+  const T* gp = at<T>(g, b, h, n);
+  float acc = 0.f;
+  for (int c0 = sub * 8; c0 < d; c0 += 128) {
+    const T8 ov = *(const T8*)(op + c0);
+    const T8 gv = *(const T8*)(gp + c0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)ov[e], (float)gv[e], acc);
+  }
+  return acc;
+}
+
+template <typename T, typename T8>
+__device__ __forceinline__ void store_scaled8(T* dst, f32x4 x0, f32x4 x1, float scale) {
+  T8 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[e] = (T)(x0[e] * scale);
+    y[4 + e] = (T)(x1[e] * scale);
+  }
+  *(T8*)dst = y;
+}
+
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
   const int sub = threadIdx.x & 15;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
@@ -30,15 +57,10 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
     const int rem = (int)(row - b * HN);
     const int h = rem / a.N, n = rem - h * a.N;
     float acc = 0.f;
-    if (a.bf16) {
-      const bf16* op = at<bf16>(a.o, b, h, n);
-      const bf16* gp = at<bf16>(a.dout, b, h, n);
-      for (int c0 = sub * 8; c0 < a.d; c0 += 128) {
-        const bf16x8 ov = *(const bf16x8*)(op + c0);
-        const bf16x8 gv = *(const bf16x8*)(gp + c0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)ov[e], (float)gv[e], acc);
-      }
+    if (a.dtype == 1) {
+      acc = row_dot16<bf16, bf16x8>(a.o, a.dout, b, h, n, a.d, sub);
+    } else if (a.dtype == 2) {
+      acc = row_dot16<f16, f16x8>(a.o, a.dout, b, h, n, a.d, sub);
     } else {
       const float* op = at<float>(a.o, b, h, n);
       const float* gp = at<float>(a.dout, b, h, n);
@@ -72,13 +94,10 @@ __global__ void __launch_bounds__(256) dq_convert_kernel(PrepArgs a) {
     const int h = rem / a.N, n = rem - h * a.N;
     const f32x4* src = (const f32x4*)(a.dq_acc + row * a.d + c0);
     const f32x4 x0 = src[0], x1 = src[1];
-    bf16x8 y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      y[e] = (bf16)(x0[e] * a.sm_scale);
-      y[4 + e] = (bf16)(x1[e] * a.sm_scale);
-    }
-    *(bf16x8*)(at<bf16>(a.dq, b, h, n) + c0) = y;
+    if (a.dtype == 2)
+      store_scaled8<f16, f16x8>(at<f16>(a.dq, b, h, n) + c0, x0, x1, a.sm_scale);
+    else
+      store_scaled8<bf16, bf16x8>(at<bf16>(a.dq, b, h, n) + c0, x0, x1, a.sm_scale);
   }
 }
 

@@ -24,7 +24,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str                 # "f32" or "bf16"
+    dtype: str                 # "f32", "bf16" or "f16"
     causal: bool = False
     window_left: int = -1
     window_right: int = -1
@@ -59,6 +59,9 @@ WORKLOADS = {
                                     notes="two-sided window |i-j| < 1024, dropout 0.1"),
     "long_causal_bf16": Workload("long_causal_bf16", 1, 8, 32768, 128, "bf16",
                                  causal=True, seed=1005),
+    "train_causal_f16": Workload("train_causal_f16", 4, 16, 4096, 128, "f16",
+                                 causal=True, seed=1006,
+                                 notes="the training shape in fp16"),
 }
 
 
@@ -77,8 +80,8 @@ def bf16_bits_to_f32(bits):
 def make_tensors(shape, dtype, seed, names=("q", "k", "v", "do")):
     """Draw the named tensors in order from PCG64(seed).
 
-    Returns {name: fp32 array of the exact stored values} and, for bf16,
-    {name + "_bits": uint16 bit patterns} for upload to the device.
+    Returns {name: fp32 array of the exact stored values} and, for bf16 and
+    fp16, {name + "_bits": uint16 bit patterns} for upload to the device.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {}
@@ -88,6 +91,10 @@ def make_tensors(shape, dtype, seed, names=("q", "k", "v", "do")):
             bits = round_to_bf16_bits(x)
             out[name + "_bits"] = bits
             out[name] = bf16_bits_to_f32(bits)
+        elif dtype == "f16":
+            h = x.astype(np.float16)  # round to nearest even
+            out[name + "_bits"] = h.view(np.uint16)
+            out[name] = h.astype(np.float32)
         elif dtype == "f32":
             out[name] = x
         else:

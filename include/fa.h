@@ -63,7 +63,8 @@ typedef enum fa_status {
 
 typedef enum fa_dtype {
   FA_DTYPE_F32 = 0,   /* fp32 inputs/outputs, fp32 arithmetic */
-  FA_DTYPE_BF16 = 1   /* bf16 inputs/outputs, bf16 MFMA with fp32 accumulation */
+  FA_DTYPE_BF16 = 1,  /* bf16 inputs/outputs, bf16 MFMA with fp32 accumulation */
+  FA_DTYPE_F16 = 2    /* fp16 inputs/outputs, fp16 MFMA with fp32 accumulation */
 } fa_dtype;
 
 /* One tensor of logical shape [B, H, N, d]; element (b, h, n, c) lives at
@@ -76,11 +77,11 @@ typedef struct fa_tensor {
 } fa_tensor;
 
 /* Flags and sizes of one attention call.
- *   dtype         FA_DTYPE_F32 or FA_DTYPE_BF16
+ *   dtype         FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16
  *   batch, heads  B, H >= 1
  *   seqlen        1 <= N <= 2^21 (queries and keys have the same length);
  *                 B * H * ceil(N / 64) must stay below 2^31
- *   head_dim      d: bf16 supports 64 and 128; fp32 supports 1..128
+ *   head_dim      d: bf16 and fp16 support 64 and 128; fp32 supports 1..128
  *   sm_scale      S = sm_scale * Q K^T (the pages use 1/sqrt(d)); any finite
  *                 value, 0 included
  *   causal        non-zero: key j is hidden from query i when j > i

@@ -86,6 +86,8 @@ VOID = ctypes.c_void_p
     (dict(shape=(0, 4, 16, 64)), 1),
     (dict(shape=(1, 4, 0, 64)), 1),
     (dict(shape=(1, 4, 16, 96)), 2),               # bf16 head dims are 64 and 128
+    (dict(shape=(1, 4, 16, 96), dtype=2), 2),      # fp16 likewise
+    (dict(dtype=3), 2),
     (dict(shape=(1, 4, 16, 256), dtype=fa.FA_DTYPE_F32), 2),
     (dict(sm_scale=math.inf), 1),
     (dict(window=(-2, -1)), 1),
@@ -138,6 +140,8 @@ def test_workspace_bytes(lib):
     assert fa.fa_bwd_workspace_bytes(_params(dtype=9)) == 0
     # fp32 never takes the atomic dQ path
     assert fa.fa_bwd_workspace_bytes(_params(shape=(2, 3, 100, 128), dtype=fa.FA_DTYPE_F32)) == 0
+    # fp16 has the same atomic mode as bf16
+    assert fa.fa_bwd_workspace_bytes(_params(shape=(2, 3, 100, 64), dtype=fa.FA_DTYPE_F16)) == 4 * 2 * 3 * 100 * 64
 
 
 def _no_gpu():

@@ -73,6 +73,31 @@ def test_ragged_bf16(B, H, N, d, causal, window, p, deterministic):
                           seed=7 + N + d), deterministic)
 
 
+# fp16: the same kernels compiled for fp16 (no workload on the pages uses it)
+F16 = [
+    (1, 2, 77, 64, True, (-1, -1), 0.0),
+    (2, 2, 300, 128, True, (-1, -1), 0.0),
+    (1, 2, 1000, 64, False, (100, 37), 0.0),
+    (1, 2, 600, 128, True, (-1, -1), 0.1),
+    (1, 1, 900, 64, False, (64, 64), 0.3),
+]
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("B,H,N,d,causal,window,p", F16)
+def test_ragged_fp16(B, H, N, d, causal, window, p, deterministic):
+    rep = _run_and_compare(Case(B, H, N, d, "f16", causal=causal, window=window, dropout_p=p,
+                                seed=11 + N + d), deterministic)
+    print("[gpu] errors", {k: tuple(float(f"{x:.3g}") for x in v) for k, v in rep.items()}, flush=True)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_train_causal_fp16_sampled_heads(deterministic):
+    rep = _run_and_compare(Case(4, 16, 4096, 128, "f16", causal=True, seed=1006), deterministic,
+                           heads=[(0, 0), (3, 15)])
+    print("[gpu] errors", {k: tuple(float(f"{x:.3g}") for x in v) for k, v in rep.items()}, flush=True)
+
+
 @pytest.mark.parametrize("B,H,N,d,causal,window,p", [
     (1, 2, 1, 32, False, (-1, -1), 0.0),
     (2, 2, 100, 40, True, (-1, -1), 0.0),
