@@ -13,13 +13,13 @@
 //                  recomputation trick"), forms dS = P * (dP - D) with the
 //                  pre-pass scalar D, and accumulates dV += P~^T dO and
 //                  dK += dS^T Q in fp32 registers, written once at the end.
-//  dkdv_kernel     KV-outer for atomic mode, 4 waves (32 keys each, K and V
-//                  in registers): the same work, plus dS K added into an
-//                  fp32 dQ accumulator with device atomics.
-//  dq_kernel       Q-outer: one workgroup owns 128 queries (32 per wave) and
-//                  streams 32-key blocks through a ring of three LDS
-//                  buffers, recomputing S, P, dP, dS to accumulate dQ = dS K
-//                  in registers: the deterministic, atomic-free dQ.
+//  dkdv_atomic_kernel  KV-outer for atomic mode, 4 waves (32 keys each, K
+//                  and V in registers): the same work, plus dS K added into
+//                  an fp32 dQ accumulator with device atomics.
+//  dq_kernel       Q-outer: 32 queries per wave (8 waves for d = 128, 4 for
+//                  d = 64) streaming 32-key blocks through a ring of three
+//                  LDS buffers, recomputing S, P, dP, dS to accumulate
+//                  dQ = dS K in registers: the deterministic, atomic-free dQ.
 //
 // Layout in LDS: Q, dO, K, V tiles are row-major 16-bit with a padded row
 // stride.  The k-inside-lane operands of the dV/dK/dQ products are read
@@ -217,15 +217,15 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
   for (int n = 0; n < DT; ++n) dk_acc[n] = mfma32x32x16(da[1], b1[n], dk_acc[n]);
 }
 
-// ---------------------------------------------------------------- KV-outer
+// ---------------------------------------------------- KV-outer, atomic dQ
 
-template <int D, bool ATOMIC>
-__global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
+template <int D>
+__global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) e16 sQ[2][C::BR * C::LD];
   __shared__ __attribute__((aligned(16))) e16 sO[2][C::BR * C::LD];
-  __shared__ __attribute__((aligned(16))) e16 sK[ATOMIC ? C::BC * C::LD : 8];
-  __shared__ __attribute__((aligned(16))) e16 sT[ATOMIC ? C::BC * C::LDS_T : 8];
+  __shared__ __attribute__((aligned(16))) e16 sK[C::BC * C::LD];
+  __shared__ __attribute__((aligned(16))) e16 sT[C::BC * C::LDS_T];
   __shared__ __attribute__((aligned(16))) float sL[2][C::BR];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BR];
 
@@ -258,14 +258,13 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
       vreg[t] = ok ? load8(vp + 16 * t + 8 * g) : zero8();
     }
   }
-  if (ATOMIC) {
+  // the block's K rows, row-major in LDS: B operand of dQ = dS K
 #pragma unroll
-    for (int x = 0; x < C::BC * C::CH / C::NT; ++x) {
-      const int chunk = tid + x * C::NT;
-      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int kr = kv0 + row;
-      store8(sK + row * C::LD + col, kr < N ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
-    }
+  for (int x = 0; x < C::BC * C::CH / C::NT; ++x) {
+    const int chunk = tid + x * C::NT;
+    const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+    const int kr = kv0 + row;
+    store8(sK + row * C::LD + col, kr < N ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
   }
 
   const int64_t row_base = (int64_t)bh * N;
@@ -373,19 +372,17 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
         da0 = zero8();
         da1 = zero8();
       }
-      if (ATOMIC) {
-        // dS^T of this wave's keys into LDS: sT[key][query]
+      // dS^T of this wave's keys into LDS: sT[key][query]
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const e16x8 src = rr < 2 ? da0 : da1;
-          const int s0 = (rr & 1) * 4;
-          const e16x4 v4 = {src[s0], src[s0 + 1], src[s0 + 2], src[s0 + 3]};
-          *(e16x4*)(sT + (32 * w + c) * C::LDS_T + 32 * qt + 8 * rr + 4 * g) = v4;
-        }
+      for (int rr = 0; rr < 4; ++rr) {
+        const e16x8 src = rr < 2 ? da0 : da1;
+        const int s0 = (rr & 1) * 4;
+        const e16x4 v4 = {src[s0], src[s0 + 1], src[s0 + 2], src[s0 + 3]};
+        *(e16x4*)(sT + (32 * w + c) * C::LDS_T + 32 * qt + 8 * rr + 4 * g) = v4;
       }
     }
 
-    if (ATOMIC) {
+    {
       lds_barrier();
       // dQ partial of the 64 queries over the block's 128 keys
       constexpr int MT = D == 128 ? 2 : 1;  // 32-query tiles per wave
@@ -415,8 +412,6 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
           if (qr < N) unsafeAtomicAdd(a.dq_acc + (row_base + qr) * D + 32 * nt + c, dq[mi][r]);
         }
       }
-    } else if (has_next) {
-      store_tile(buf ^ 1);
     }
     lds_barrier();
   }
@@ -885,7 +880,7 @@ hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
     hipLaunchKernelGGL(a.m.dropout ? (dq_kernel<D, true>) : (dq_kernel<D, false>), grid_q, dim3(QCfg<D>::NT),
                        0, s, a);
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<D, true>), grid_kv, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((dkdv_atomic_kernel<D>), grid_kv, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
