@@ -19,9 +19,9 @@
  *   - Tensors Q, K, V, O, dO, dQ, dK, dV are described by fa_tensor: a device
  *     pointer and element strides for the batch, head and sequence axes; the
  *     head-dim axis has stride 1.  [B,H,N,d] contiguous and [B,N,H,d] are
- *     both expressible.  bf16 tensors need a 16-byte aligned pointer and
- *     strides that are multiples of 8 elements; fp32 tensors need 4-byte
- *     alignment.
+ *     both expressible.  bf16 and fp16 tensors need a 16-byte aligned
+ *     pointer and strides that are multiples of 8 elements, and fit each
+ *     row stride in 32 bits of bytes; fp32 tensors need 4-byte alignment.
  *   - L (lse), D (delta) are fp32, [B,H,N] contiguous.  L is the natural log
  *     of sum_j exp(S_ij) over the visible keys of row i, with
  *     S = sm_scale * Q K^T.
@@ -93,10 +93,12 @@ typedef struct fa_tensor {
  *                 kept weights are scaled by 1/(1 - p).  Requires B, H, N
  *                 <= 65536 when p > 0.
  *   seed, offset  Philox4x32-10 stream of the dropout mask: key = seed,
- *                 counter = (offset, (i << 16) | j, (b << 16) | h); weight
- *                 (b, h, i, j) is kept iff word 0 >= ceil(p * 2^32).
+ *                 one block per four keys j4 = j - j % 4, counter =
+ *                 (offset, (i << 16) | j4, (b << 16) | h); weight
+ *                 (b, h, i, j) is kept iff word j % 4 >= ceil(p * 2^32).
  *   deterministic non-zero: dQ by a separate Q-outer kernel, bit-identical
- *                 run to run; zero: dQ by fp32 atomics into a workspace.
+ *                 run to run; zero: for bf16/fp16, dQ by fp32 atomics into
+ *                 a workspace (fp32 computes dQ without atomics either way).
  */
 typedef struct fa_params {
   int32_t dtype;
@@ -134,13 +136,13 @@ fa_status fa_fwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
  * accumulated in fp32 ("FlashAttention backward", "The gradients, and the
  * one scalar that makes them local").  delta: fp32 [B,H,N] output.
  * dq_acc: the fp32 workspace of fa_bwd when fa_bwd_workspace_bytes(params)
- * is not 0 (bf16 with deterministic == 0), which this call then zeroes and
+ * is not 0 (bf16/fp16 with deterministic == 0), which this call then zeroes and
  * which that fa_bwd requires zeroed; NULL there skips the zeroing.  For
  * every other params it is ignored and never written (may be NULL). */
 fa_status fa_bwd_preprocess(const fa_params* params, fa_tensor o, fa_tensor dout,
                             float* delta, float* dq_acc, void* stream);
 
-/* Bytes of fp32 workspace fa_bwd needs: 4*B*H*N*d for bf16 with
+/* Bytes of fp32 workspace fa_bwd needs: 4*B*H*N*d for bf16/fp16 with
  * deterministic == 0 (the dQ accumulator, [B,H,N,d] contiguous), else 0
  * (also 0 when params are invalid). */
 size_t fa_bwd_workspace_bytes(const fa_params* params);
