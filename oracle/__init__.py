@@ -8,7 +8,8 @@ only thing both sides consume is the seeded synthetic input data, produced
 by a separate module that holds none of the method's arithmetic.
 
 Contents
-  attention  plain forward / backward with S, P, dS materialised (numpy fp64)
+  attention  plain forward / backward with S, P, dS materialised (numpy fp64),
+             for equal or different query/key lengths and packed varlen batches
   philox     Philox4x32-10 and the dropout keep mask (numpy uint64)
 
 Parity pins (tests/test_oracle_*.py): finite differences, torch fp64 autograd
@@ -34,6 +35,7 @@ from .attention import (  # noqa: F401
     materialised_p_bytes,
     saved_state_bytes,
     valid_mask,
+    varlen_backward,
 )
 from .philox import (  # noqa: F401
     dropout_keep,

@@ -22,7 +22,14 @@ Everything is computed from the definitions on the pages, in binary64:
   dQ = sm_scale * dS K;  dK = sm_scale * dS^T Q
 
 The pages write the scale as 1/sqrt(d); a general sm_scale multiplies S and
-the dQ/dK products in the same places.  Dropout is differentiated by the
+the dQ/dK products in the same places.
+
+Queries and keys may differ in number (Nq, Nk).  The pages fix no alignment
+for that case; this oracle aligns the last query with the last key, so query
+i stands at key position i + Nk - Nq for the causal and window tests.  A row
+that then sees no key has an empty softmax sum: L = log 0 = -inf, P = 0,
+O = 0, and every gradient through it is 0.  Variable-length batches
+(varlen_backward) are each sequence on its own, with its batch index b.  Dropout is differentiated by the
 chain rule through P~ (the pages do not derive it); the same D is correct
 because sum_j P_ij dP_ij = sum_j P~_ij (dO_i . V_j) = dO_i . O_i.
 
@@ -52,12 +59,14 @@ class Spec:
     offset: int = 0
 
 
-def valid_mask(rows, cols, spec):
+def valid_mask(rows, cols, spec, shift=0):
     """valid(i, j): key j is visible to query i ("Lecture 7", "Mask behaviour").
 
-    Causal hides j > i; a window keeps i - window_left <= j <= i + window_right.
+    Query i stands at key position i + shift (shift = Nk - Nq).  Causal hides
+    keys after that position; a window keeps window_left keys before it and
+    window_right keys after it.
     """
-    i = np.asarray(rows, dtype=np.int64).reshape(-1, 1)
+    i = np.asarray(rows, dtype=np.int64).reshape(-1, 1) + shift
     j = np.asarray(cols, dtype=np.int64).reshape(1, -1)
     ok = np.ones((i.shape[0], j.shape[1]), dtype=bool)
     if spec.causal:
@@ -69,9 +78,9 @@ def valid_mask(rows, cols, spec):
     return ok
 
 
-def _key_range(rows, n, spec):
+def _key_range(rows, n, spec, shift=0):
     """Smallest [lo, hi) holding every key visible to at least one of rows."""
-    r0, r1 = int(np.min(rows)), int(np.max(rows))
+    r0, r1 = int(np.min(rows)) + shift, int(np.max(rows)) + shift
     lo, hi = 0, n
     if spec.causal:
         hi = min(hi, r1 + 1)
@@ -79,6 +88,7 @@ def _key_range(rows, n, spec):
         lo = max(lo, r0 - spec.window_left)
     if spec.window_right >= 0:
         hi = min(hi, r1 + spec.window_right + 1)
+    lo = min(lo, n)
     return lo, max(lo, hi)
 
 
@@ -91,22 +101,29 @@ def _row_groups(n, chunk):
 def head_rows_forward(q, k, v, spec, b, h, rows):
     """Forward quantities of one head for the query rows `rows`.
 
-    q, k, v: [N, d] arrays (any float dtype; widened to fp64).
+    q: [Nq, d], k, v: [Nk, d] arrays (any float dtype; widened to fp64).
     Returns a dict with the key range and the materialised S, P, Z, P~, O, L.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     n = k.shape[0]
-    lo, hi = _key_range(rows, n, spec)
+    shift = n - q.shape[0]
+    lo, hi = _key_range(rows, n, spec, shift)
     cols = np.arange(lo, hi)
-    ok = valid_mask(rows, cols, spec)
+    ok = valid_mask(rows, cols, spec, shift)
     s = spec.sm_scale * (q[rows] @ k[lo:hi].T)
     s = np.where(ok, s, -np.inf)
-    m = s.max(axis=1, keepdims=True)
-    ell = np.exp(s - m).sum(axis=1, keepdims=True)
-    lse = m + np.log(ell)
-    p = np.exp(s - lse)  # exactly 0 where the score is -inf
+    # rows that see no key keep L = -inf and P = 0 (an empty sum)
+    live = ok.any(axis=1)
+    lse = np.full((len(rows), 1), -np.inf)
+    p = np.zeros_like(s)
+    if live.any():
+        sl = s[live]
+        m = sl.max(axis=1, keepdims=True)
+        ell = np.exp(sl - m).sum(axis=1, keepdims=True)
+        lse[live] = m + np.log(ell)
+        p[live] = np.exp(sl - lse[live])  # exactly 0 where the score is -inf
     if spec.dropout_p > 0.0:
         z = philox.dropout_keep(spec.seed, spec.offset, b, h, rows, cols, spec.dropout_p)
         p_drop = p * z / (1.0 - spec.dropout_p)
@@ -119,7 +136,7 @@ def head_rows_forward(q, k, v, spec, b, h, rows):
 
 
 def head_forward(q, k, v, spec, b=0, h=0, chunk=None):
-    """O [N, d] and L [N] of one head."""
+    """O [Nq, d] and L [Nq] of one head."""
     n, dv = q.shape[0], v.shape[1]
     o = np.zeros((n, dv))
     lse = np.zeros(n)
@@ -162,8 +179,8 @@ def head_backward(q, k, v, do, spec, b=0, h=0, chunk=None):
     """dQ, dK, dV (and O, L, D) of one head, from the definitions above."""
     n = q.shape[0]
     dq = np.zeros((n, q.shape[1]))
-    dk = np.zeros((n, k.shape[1]))
-    dv = np.zeros((n, v.shape[1]))
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
     o = np.zeros((n, v.shape[1]))
     lse = np.zeros(n)
     delta = np.zeros(n)
@@ -185,7 +202,7 @@ def head_delta(o, do):
 
 
 def forward(q, k, v, spec, heads=None, chunk=None):
-    """O [B,H,N,d] and L [B,H,N] for all heads (or only the listed (b, h))."""
+    """O [B,H,Nq,d] and L [B,H,Nq] for all heads (or only the listed (b, h))."""
     bsz, nh, n, _ = q.shape
     o = np.zeros(q.shape[:3] + (v.shape[3],))
     lse = np.zeros((bsz, nh, n))
@@ -195,13 +212,13 @@ def forward(q, k, v, spec, heads=None, chunk=None):
 
 
 def backward(q, k, v, do, spec, heads=None, chunk=None):
-    """dQ, dK, dV, O, L, D for [B,H,N,d] inputs (all heads or the listed ones).
+    """dQ, dK, dV, O, L, D for [B,H,Nq,d] queries and [B,H,Nk,d] keys/values.
 
-    Heads that are not listed are left at zero.
+    All heads or the listed ones; heads that are not listed are left at zero.
     """
     bsz, nh, n, d = q.shape
-    out = {"dq": np.zeros((bsz, nh, n, d)), "dk": np.zeros((bsz, nh, n, d)),
-           "dv": np.zeros((bsz, nh, n, v.shape[3])), "o": np.zeros((bsz, nh, n, v.shape[3])),
+    out = {"dq": np.zeros((bsz, nh, n, d)), "dk": np.zeros(k.shape),
+           "dv": np.zeros(v.shape), "o": np.zeros((bsz, nh, n, v.shape[3])),
            "lse": np.zeros((bsz, nh, n)), "delta": np.zeros((bsz, nh, n))}
     for b, h in (heads if heads is not None else np.ndindex(bsz, nh)):
         r = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], spec, b, h, chunk)
@@ -210,19 +227,49 @@ def backward(q, k, v, do, spec, heads=None, chunk=None):
     return out
 
 
-def dropout_mask(spec, b, h, n):
-    """The full N x N keep mask Z of head (b, h) (uint8), for small N."""
-    idx = np.arange(n)
-    return philox.dropout_keep(spec.seed, spec.offset, b, h, idx, idx, spec.dropout_p)
+def varlen_backward(q, k, v, do, cu_q, cu_k, spec, chunk=None):
+    """The backward of a packed variable-length batch, one sequence at a time.
+
+    q, do: [total_q, H, d]; k, v: [total_k, H, d]; sequence b owns rows
+    cu_q[b]:cu_q[b+1] of q and cu_k[b]:cu_k[b+1] of k.  Returns packed O, dQ,
+    dK, dV and L, D as [B, H, max query length] (NaN past each length).
+    """
+    bsz = len(cu_q) - 1
+    nh = q.shape[1]
+    max_q = max(int(cu_q[b + 1] - cu_q[b]) for b in range(bsz))
+    out = {"dq": np.zeros(q.shape), "dk": np.zeros(k.shape), "dv": np.zeros(v.shape),
+           "o": np.zeros(q.shape[:2] + (v.shape[2],)),
+           "lse": np.full((bsz, nh, max_q), np.nan), "delta": np.full((bsz, nh, max_q), np.nan)}
+    for b in range(bsz):
+        qs, ks = slice(int(cu_q[b]), int(cu_q[b + 1])), slice(int(cu_k[b]), int(cu_k[b + 1]))
+        nq = qs.stop - qs.start
+        for h in range(nh):
+            if nq == 0:
+                continue
+            r = head_backward(q[qs, h], k[ks, h], v[ks, h], do[qs, h], spec, b, h, chunk)
+            for name in ("dq", "o"):
+                out[name][qs, h] = r[name]
+            for name in ("dk", "dv"):
+                out[name][ks, h] = r[name]
+            out["lse"][b, h, :nq] = r["lse"]
+            out["delta"][b, h, :nq] = r["delta"]
+    return out
 
 
-def credited_flops(bsz, nh, n, d, spec):
+def dropout_mask(spec, b, h, n, n_k=None):
+    """The full Nq x Nk keep mask Z of head (b, h) (uint8), for small sizes."""
+    return philox.dropout_keep(spec.seed, spec.offset, b, h, np.arange(n),
+                               np.arange(n if n_k is None else n_k), spec.dropout_p)
+
+
+def credited_flops(bsz, nh, n, d, spec, n_k=None):
     """10 * d per visible (b, h, i, j): the five N x N x d products of the backward."""
+    n_k = n if n_k is None else n_k
     visible = 0
     step = 4096
     for start in range(0, n, step):
         rows = np.arange(start, min(n, start + step))
-        visible += int(valid_mask(rows, np.arange(n), spec).sum())
+        visible += int(valid_mask(rows, np.arange(n_k), spec, n_k - n).sum())
     return 10.0 * d * visible * bsz * nh
 
 

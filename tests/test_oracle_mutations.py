@@ -25,9 +25,20 @@ MUTANTS = {
     "dv_without_dropout": ("f[\"p_drop\"].T @ do[rows]", "f[\"p\"].T @ do[rows]"),
     "dp_without_dropout": ("dp = dp * f[\"z\"] / (1.0 - spec.dropout_p)", "dp = dp"),
     "dq_uses_v": ("(ds @ k[lo:hi])", "(ds @ v[lo:hi])"),
-    "lse_without_max": ("lse = m + np.log(ell)", "lse = np.log(ell)"),
+    "lse_without_max": ("lse[live] = m + np.log(ell)", "lse[live] = np.log(ell)"),
     "causal_off_by_one": ("ok &= j <= i", "ok &= j < i + 2"),
     "window_wrong_side": ("ok &= j >= i - spec.window_left", "ok &= j >= i - spec.window_left - 1"),
+}
+
+# Mistakes in the alignment of unequal query and key lengths
+UNEQUAL_MUTANTS = {
+    "shift_sign": ("shift = n - q.shape[0]", "shift = q.shape[0] - n"),
+    "shift_left_out_of_mask": ("ok = valid_mask(rows, cols, spec, shift)",
+                               "ok = valid_mask(rows, cols, spec)"),
+    "shift_left_out_of_key_range": ("lo, hi = _key_range(rows, n, spec, shift)",
+                                    "lo, hi = _key_range(rows, n, spec)"),
+    "empty_rows_get_zero_lse": ("lse = np.full((len(rows), 1), -np.inf)",
+                                "lse = np.full((len(rows), 1), 0.0)"),
 }
 
 
@@ -79,8 +90,48 @@ def _pins_pass(mod):
     return True
 
 
+def _unequal_pins_pass(mod):
+    """A compact run of the unequal-length pin: torch's lower-right causal bias."""
+    import warnings
+    from torch.nn.attention.bias import causal_lower_right
+    rng = np.random.default_rng(9)
+    d = 4
+    for nq, nk in ((5, 11), (11, 5)):
+        q, do = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+        k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+        r = mod.head_backward(q, k, v, do, mod.Spec(sm_scale=0.6, causal=True))
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            bias = causal_lower_right(nq, nk)
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq.view(1, 1, nq, d), tk.view(1, 1, nk, d), tv.view(1, 1, nk, d), attn_mask=bias,
+            scale=0.6).view(nq, d)
+        o.backward(torch.tensor(do))
+        mask = bias._materialize(device="cpu").view(nq, nk)
+        lse = torch.logsumexp(((tq @ tk.T) * 0.6).masked_fill(~mask, float("-inf")), -1)
+        if not np.array_equal(np.isneginf(r["lse"]), np.isneginf(lse.detach().numpy())):
+            return False
+        live = np.isfinite(r["lse"])
+        if not np.allclose(r["lse"][live], lse.detach().numpy()[live], rtol=1e-10):
+            return False
+        if not np.allclose(r["o"], o.detach().numpy(), rtol=1e-9, atol=1e-10):
+            return False
+        for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+            if not np.allclose(r[name], t.grad.numpy(), rtol=1e-9, atol=1e-10):
+                return False
+    return True
+
+
 def test_unmutated_oracle_passes_compact_pins():
     assert _pins_pass(_load_mutant("", ""))
+    assert _unequal_pins_pass(_load_mutant("", ""))
+
+
+@pytest.mark.parametrize("name", list(UNEQUAL_MUTANTS))
+def test_unequal_length_mutant_is_caught(name):
+    old, new = UNEQUAL_MUTANTS[name]
+    assert not _unequal_pins_pass(_load_mutant(old, new)), name
 
 
 @pytest.mark.parametrize("name", list(MUTANTS))
