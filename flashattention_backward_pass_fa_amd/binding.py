@@ -7,8 +7,11 @@ package directory; if it is missing the call raises (there is no fallback).
 Low level: fa_abi_version, fa_status_string, fa_fwd, fa_bwd_preprocess,
 fa_bwd_workspace_bytes, fa_bwd, fa_debug_dropout_mask take FaParams /
 FaTensor structures and raw device pointers, exactly like the C functions.
-High level: forward(...) and backward(...) take torch tensors on the GPU,
-allocate the outputs with torch and enqueue on torch's current stream.
+High level: forward(...) and backward(...) take [B, H, N, d] torch tensors
+on the GPU (queries and keys may differ in N), forward_varlen(...) and
+backward_varlen(...) packed [total, H, d] tensors with cumulative sequence
+offsets; they allocate the outputs with torch and enqueue on torch's
+current stream.
 """
 
 import ctypes
@@ -21,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F16 = 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS_NAMES = {
     0: "FA_SUCCESS",
@@ -43,11 +46,13 @@ class FaTensor(ctypes.Structure):
 
 class FaParams(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
-                ("seqlen", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
-                ("deterministic", ctypes.c_int32), ("dropout_p", ctypes.c_double),
-                ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+                ("seqlen", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32), ("deterministic", ctypes.c_int32),
+                ("dropout_p", ctypes.c_double), ("seed", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64), ("cu_seqlens_q", ctypes.c_void_p),
+                ("cu_seqlens_k", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -135,20 +140,33 @@ def fa_debug_dropout_mask(params, b, h, mask, stream):
 # ------------------------------------------------------ torch-facing helpers
 
 def make_params(shape, dtype, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0,
-                seed=0, offset=0, deterministic=False):
-    """FaParams for a [B, H, N, d] problem; sm_scale None means 1/sqrt(d)."""
+                seed=0, offset=0, deterministic=False, seqlen_k=None, cu_seqlens_q=None,
+                cu_seqlens_k=None):
+    """FaParams for a [B, H, Nq, d] problem with Nk = seqlen_k keys (default Nq).
+
+    sm_scale None means 1/sqrt(d).  cu_seqlens_q / cu_seqlens_k: device
+    addresses (ints) of the varlen offset arrays, or None.
+    """
     bsz, nh, n, d = shape
-    return FaParams(dtype=dtype, batch=bsz, heads=nh, seqlen=n, head_dim=d,
+    return FaParams(dtype=dtype, batch=bsz, heads=nh, seqlen=n,
+                    seqlen_k=n if seqlen_k is None else int(seqlen_k), head_dim=d,
                     sm_scale=(1.0 / math.sqrt(d)) if sm_scale is None else float(sm_scale),
                     causal=1 if causal else 0, window_left=int(window[0]),
                     window_right=int(window[1]), deterministic=1 if deterministic else 0,
-                    dropout_p=float(dropout_p), seed=int(seed), offset=int(offset))
+                    dropout_p=float(dropout_p), seed=int(seed), offset=int(offset),
+                    cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
 
 
 def tensor_arg(t):
-    """FaTensor view of a [B, H, N, d] torch tensor (d-stride must be 1)."""
+    """FaTensor view of a [B, H, N, d] tensor or a packed [total, H, d] one.
+
+    The d-stride must be 1.  A packed tensor gets batch stride 0 (varlen
+    mode ignores it).
+    """
+    if t.dim() == 3 and t.stride(2) == 1:
+        return FaTensor(t.data_ptr(), 0, t.stride(1), t.stride(0))
     if t.dim() != 4 or t.stride(3) != 1:
-        raise ValueError("expected a [B, H, N, d] tensor with unit stride on d")
+        raise ValueError("expected a [B, H, N, d] or [total, H, d] tensor with unit stride on d")
     return FaTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
@@ -179,7 +197,7 @@ def forward(q, k, v, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0
     """O (dtype of q) and L (fp32 [B, H, N]) of softmax attention on q, k, v."""
     import torch
     params = make_params(tuple(q.shape), _dtype_code(q), sm_scale, causal, window, dropout_p,
-                         seed, offset)
+                         seed, offset, seqlen_k=k.shape[2])
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
@@ -195,12 +213,16 @@ def backward(q, k, v, o, dout, lse, sm_scale=None, causal=False, window=(-1, -1)
     (atomic mode); allocated here when None.  delta: optional fp32 [B, H, N]
     output for D.  Returns (dq, dk, dv, delta).
     """
-    import torch
     params = make_params(tuple(q.shape), _dtype_code(q), sm_scale, causal, window, dropout_p,
-                         seed, offset, deterministic)
+                         seed, offset, deterministic, seqlen_k=k.shape[2])
+    return _backward(params, q, k, v, o, dout, lse, q.shape[:3], stream, workspace, delta)
+
+
+def _backward(params, q, k, v, o, dout, lse, delta_shape, stream, workspace, delta):
+    import torch
     st = _stream(stream)
     if delta is None:
-        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        delta = torch.empty(delta_shape, dtype=torch.float32, device=q.device)
     ws_bytes = fa_bwd_workspace_bytes(params)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device)
@@ -214,12 +236,62 @@ def backward(q, k, v, o, dout, lse, sm_scale=None, causal=False, window=(-1, -1)
     return dq, dk, dv, delta
 
 
-def debug_dropout_mask(shape, b, h, dropout_p, seed, offset=0, device="cuda", stream=None):
-    """The N x N keep mask (uint8) of head (b, h), computed on the GPU."""
+def _varlen_params(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale, causal,
+                   window, dropout_p, seed, offset, deterministic=False):
     import torch
-    params = make_params(shape, FA_DTYPE_F32, None, False, (-1, -1), dropout_p, seed, offset)
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous() or cu.device != q.device:
+            raise ValueError("cu_seqlens must be contiguous int32 vectors on the tensors' device")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same B + 1 >= 2 entries")
+    bsz = cu_seqlens_q.numel() - 1
+    return make_params((bsz, q.shape[1], int(max_seqlen_q), q.shape[2]), _dtype_code(q), sm_scale,
+                       causal, window, dropout_p, seed, offset, deterministic,
+                       seqlen_k=int(max_seqlen_k), cu_seqlens_q=cu_seqlens_q.data_ptr(),
+                       cu_seqlens_k=cu_seqlens_k.data_ptr())
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale=None,
+                   causal=False, window=(-1, -1), dropout_p=0.0, seed=0, offset=0, stream=None):
+    """Packed variable-length forward.
+
+    q: [total_q, H, d]; k, v: [total_k, H, d]; sequence b owns rows
+    cu_seqlens_q[b]:cu_seqlens_q[b+1] of q (int32 device tensors of B + 1
+    entries).  Returns O [total_q, H, d] and L [B, H, max_seqlen_q] (entries
+    past a sequence's length are not written).
+    """
+    import torch
+    params = _varlen_params(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale,
+                            causal, window, dropout_p, seed, offset)
+    o = torch.empty_like(q)
+    lse = torch.empty((params.batch, q.shape[1], params.seqlen), dtype=torch.float32,
+                      device=q.device)
+    _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
+                  ctypes.c_void_p(lse.data_ptr()), _stream(stream)), "fa_fwd")
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0, seed=0, offset=0,
+                    deterministic=False, stream=None, workspace=None, delta=None):
+    """Packed variable-length backward; tensors as in forward_varlen.
+
+    Returns (dq, dk, dv, delta) with delta [B, H, max_seqlen_q].
+    """
+    params = _varlen_params(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale,
+                            causal, window, dropout_p, seed, offset, deterministic)
+    return _backward(params, q, k, v, o, dout, lse, (params.batch, q.shape[1], params.seqlen),
+                     stream, workspace, delta)
+
+
+def debug_dropout_mask(shape, b, h, dropout_p, seed, offset=0, device="cuda", stream=None,
+                       seqlen_k=None):
+    """The Nq x Nk keep mask (uint8) of head (b, h), computed on the GPU."""
+    import torch
+    params = make_params(shape, FA_DTYPE_F32, None, False, (-1, -1), dropout_p, seed, offset,
+                         seqlen_k=seqlen_k)
     n = shape[2]
-    mask = torch.empty((n, n), dtype=torch.uint8, device=device)
+    mask = torch.empty((n, params.seqlen_k), dtype=torch.uint8, device=device)
     _check(fa_debug_dropout_mask(params, b, h, ctypes.c_void_p(mask.data_ptr()), _stream(stream)),
            "fa_debug_dropout_mask")
     return mask

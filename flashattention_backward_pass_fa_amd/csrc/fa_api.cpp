@@ -30,11 +30,17 @@ fa_status check_params(const fa_params* p) {
   if (!p) return FA_ERR_INVALID_VALUE;
   if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F16)
     return FA_ERR_NOT_SUPPORTED;
-  if (p->batch < 1 || p->heads < 1 || p->seqlen < 1 || p->head_dim < 1) return FA_ERR_INVALID_VALUE;
+  if (p->batch < 1 || p->heads < 1 || p->seqlen < 1 || p->seqlen_k < 1 || p->head_dim < 1)
+    return FA_ERR_INVALID_VALUE;
   if ((int64_t)p->batch * p->heads > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
-  if (p->seqlen > kMaxSeq) return FA_ERR_NOT_SUPPORTED;
+  if (p->seqlen > kMaxSeq || p->seqlen_k > kMaxSeq) return FA_ERR_NOT_SUPPORTED;
   // the kernels number their workgroups (one per head and 64 rows) in an int
-  if ((int64_t)p->batch * p->heads * ((p->seqlen + 63) / 64) > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
+  const int64_t longest = p->seqlen > p->seqlen_k ? p->seqlen : p->seqlen_k;
+  if ((int64_t)p->batch * p->heads * ((longest + 63) / 64) > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
+  // varlen: both offset arrays or neither
+  if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_k == nullptr)) return FA_ERR_INVALID_VALUE;
+  if (p->cu_seqlens_q && (!aligned(p->cu_seqlens_q, 4) || !aligned(p->cu_seqlens_k, 4)))
+    return FA_ERR_MISALIGNED;
   if (is16(p) && p->head_dim != 64 && p->head_dim != 128) return FA_ERR_NOT_SUPPORTED;
   if (p->dtype == FA_DTYPE_F32 && p->head_dim > 128) return FA_ERR_NOT_SUPPORTED;
   if (!std::isfinite(p->sm_scale)) return FA_ERR_INVALID_VALUE;
@@ -42,10 +48,13 @@ fa_status check_params(const fa_params* p) {
   if (!(p->dropout_p >= 0.0 && p->dropout_p < 1.0)) return FA_ERR_INVALID_VALUE;
   if (p->dropout_p > 0.0) {
     if (std::ceil(p->dropout_p * 4294967296.0) > 4294967295.0) return FA_ERR_INVALID_VALUE;
-    if (p->batch > 65536 || p->heads > 65536 || p->seqlen > 65536) return FA_ERR_NOT_SUPPORTED;
+    if (p->batch > 65536 || p->heads > 65536 || p->seqlen > 65536 || p->seqlen_k > 65536)
+      return FA_ERR_NOT_SUPPORTED;
   }
   return FA_SUCCESS;
 }
+
+bool varlen(const fa_params* p) { return p->cu_seqlens_q != nullptr; }
 
 // Atomic dQ mode (16-bit dtypes, deterministic == 0) accumulates dQ in an
 // fp32 workspace; every other call has none.
@@ -53,10 +62,11 @@ bool uses_dq_acc(const fa_params* p) { return is16(p) && !p->deterministic; }
 
 fa_status check_tensor(const fa_params* p, const fa_tensor& t) {
   if (!t.ptr) return FA_ERR_INVALID_VALUE;
-  if (t.stride_b < 0 || t.stride_h < 0 || t.stride_n < 0) return FA_ERR_INVALID_VALUE;
+  const int64_t sb = varlen(p) ? 0 : t.stride_b;  // varlen ignores the batch stride
+  if (sb < 0 || t.stride_h < 0 || t.stride_n < 0) return FA_ERR_INVALID_VALUE;
   if (is16(p)) {
     if (!aligned(t.ptr, 16)) return FA_ERR_MISALIGNED;
-    if ((t.stride_b % 8) || (t.stride_h % 8) || (t.stride_n % 8)) return FA_ERR_MISALIGNED;
+    if ((sb % 8) || (t.stride_h % 8) || (t.stride_n % 8)) return FA_ERR_MISALIGNED;
     if (t.stride_n > INT32_MAX) return FA_ERR_NOT_SUPPORTED;  // row offsets are 32-bit products
   } else if (!aligned(t.ptr, 4)) {
     return FA_ERR_MISALIGNED;
@@ -76,18 +86,25 @@ fa_status check_vec(const float* v, uintptr_t align) {
     if (st_ != FA_SUCCESS) return st_;    \
   } while (0)
 
-fa::TensorView view(const fa_tensor& t) { return fa::TensorView{t.ptr, t.stride_b, t.stride_h, t.stride_n}; }
+// varlen views carry no batch stride: sequence b's rows are located by the
+// offset arrays instead
+fa::TensorView view(const fa_params* p, const fa_tensor& t) {
+  return fa::TensorView{t.ptr, varlen(p) ? 0 : t.stride_b, t.stride_h, t.stride_n};
+}
 
 fa::MaskArgs mask_args(const fa_params* p) {
   fa::MaskArgs m{};
-  m.n = p->seqlen;
+  m.nq = p->seqlen;
+  m.nk = p->seqlen_k;
   m.causal = p->causal ? 1 : 0;
-  m.wl = p->window_left;
-  m.wr = p->window_right;
-  // visible iff i - lo_off <= j <= i + hi_off; 2^30 stands for unbounded
+  // visible iff i' - window_left <= j <= i' + window_right (j <= i' if
+  // causal), with i' = i + nk - nq; the kernels add that shift per sequence.
+  // 2^30 stands for unbounded (|nk - nq| < 2^21 keeps every sum in range).
   m.lo_off = p->window_left >= 0 ? p->window_left : (1 << 30);
   m.hi_off = p->window_right >= 0 ? p->window_right : (1 << 30);
   if (p->causal && m.hi_off > 0) m.hi_off = 0;
+  m.cu_q = p->cu_seqlens_q;
+  m.cu_k = p->cu_seqlens_k;
   m.dropout = p->dropout_p > 0.0 ? 1 : 0;
   m.keep_threshold = (uint32_t)std::ceil(p->dropout_p * 4294967296.0);
   m.keep_scale = (float)(1.0 / (1.0 - p->dropout_p));
@@ -152,14 +169,15 @@ fa_status fa_fwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   if (o.ptr == q.ptr || o.ptr == k.ptr || o.ptr == v.ptr || o.ptr == (void*)lse) return FA_ERR_INVALID_VALUE;
   FA_TRY(device_ready());
   fa::FwdArgs a{};
-  a.q = view(q);
-  a.k = view(k);
-  a.v = view(v);
-  a.o = view(o);
+  a.q = view(p, q);
+  a.k = view(p, k);
+  a.v = view(p, v);
+  a.o = view(p, o);
   a.lse = lse;
   a.B = p->batch;
   a.H = p->heads;
   a.d = p->head_dim;
+  a.ln = p->seqlen;
   a.sm_scale = p->sm_scale;
   a.scale_log2 = p->sm_scale * kLog2e;
   a.m = mask_args(p);
@@ -188,10 +206,11 @@ fa_status fa_bwd_preprocess(const fa_params* p, fa_tensor o, fa_tensor dout, flo
     return FA_ERR_INVALID_VALUE;
   FA_TRY(device_ready());
   fa::PrepArgs a{};
-  a.o = view(o);
-  a.dout = view(dout);
+  a.o = view(p, o);
+  a.dout = view(p, dout);
   a.delta = delta;
   a.dq_acc = dq_acc;
+  a.cu_q = p->cu_seqlens_q;
   a.B = p->batch;
   a.H = p->heads;
   a.N = p->seqlen;
@@ -227,19 +246,20 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
     return FA_ERR_INVALID_VALUE;
   FA_TRY(device_ready());
   fa::BwdArgs a{};
-  a.q = view(q);
-  a.k = view(k);
-  a.v = view(v);
-  a.dout = view(dout);
-  a.dq = view(dq);
-  a.dk = view(dk);
-  a.dv = view(dv);
+  a.q = view(p, q);
+  a.k = view(p, k);
+  a.v = view(p, v);
+  a.dout = view(p, dout);
+  a.dq = view(p, dq);
+  a.dk = view(p, dk);
+  a.dv = view(p, dv);
   a.lse = lse;
   a.delta = delta;
   a.dq_acc = atomic ? dq_acc : nullptr;
   a.B = p->batch;
   a.H = p->heads;
   a.d = p->head_dim;
+  a.ln = p->seqlen;
   a.sm_scale = p->sm_scale;
   a.scale_log2 = p->sm_scale * kLog2e;
   a.m = mask_args(p);
@@ -249,8 +269,9 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
                                              : fa::launch_bwd16(a, !atomic, s)));
   if (atomic) {
     fa::PrepArgs c{};
-    c.dq = view(dq);
+    c.dq = view(p, dq);
     c.dq_acc = dq_acc;
+    c.cu_q = p->cu_seqlens_q;
     c.B = p->batch;
     c.H = p->heads;
     c.N = p->seqlen;
@@ -266,7 +287,8 @@ fa_status fa_debug_dropout_mask(const fa_params* p, int32_t b, int32_t h, uint8_
   FA_TRY(check_params(p));
   if (!mask) return FA_ERR_INVALID_VALUE;
   if (b < 0 || b >= p->batch || h < 0 || h >= p->heads) return FA_ERR_INVALID_VALUE;
-  if (p->seqlen > 65536 || p->batch > 65536 || p->heads > 65536) return FA_ERR_NOT_SUPPORTED;
+  if (p->seqlen > 65536 || p->seqlen_k > 65536 || p->batch > 65536 || p->heads > 65536)
+    return FA_ERR_NOT_SUPPORTED;
   FA_TRY(device_ready());
   return launched(fa::launch_dropout_mask(mask_args(p), b, h, mask, (hipStream_t)stream));
 }

@@ -65,22 +65,31 @@ __device__ __forceinline__ e16x8 zero8() {
   return z;
 }
 
-// Is every (query, key) of rows [q0, q0+nq) x keys [k0, k0+nk) visible?
-__device__ __forceinline__ bool block_full(const MaskArgs& m, int q0, int nq, int k0, int nk) {
-  bool ok = (q0 + nq <= m.n) & (k0 + nk <= m.n);
-  if (m.causal) ok &= (k0 + nk - 1 <= q0);
-  if (m.wl >= 0) ok &= (k0 >= q0 + nq - 1 - m.wl);
-  if (m.wr >= 0) ok &= (k0 + nk - 1 <= q0 + m.wr);
-  return ok;
+// Is every (query, key) of rows [q0, q0+rows) x keys [k0, k0+cols) visible?
+__device__ __forceinline__ bool block_full(const MaskArgs& m, int q0, int rows, int k0, int cols) {
+  return (q0 + rows <= m.nq) & (k0 + cols <= m.nk) & (k0 >= q0 + rows - 1 - m.lo_off) &
+         (k0 + cols - 1 <= q0 + m.hi_off);
 }
 
 // Is every (query, key) of that block hidden?
-__device__ __forceinline__ bool block_dead(const MaskArgs& m, int q0, int nq, int k0, int nk) {
-  bool dead = (q0 >= m.n) | (k0 >= m.n);
-  if (m.causal) dead |= (k0 > q0 + nq - 1);
-  if (m.wl >= 0) dead |= (k0 + nk - 1 < q0 - m.wl);
-  if (m.wr >= 0) dead |= (k0 > q0 + nq - 1 + m.wr);
-  return dead;
+__device__ __forceinline__ bool block_dead(const MaskArgs& m, int q0, int rows, int k0, int cols) {
+  return (q0 >= m.nq) | (k0 >= m.nk) | (k0 + cols - 1 < q0 - m.lo_off) |
+         (k0 > q0 + rows - 1 + m.hi_off);
+}
+
+// Specialise the call to sequence b (its lengths, mask offsets and, for
+// varlen, the packed rows it starts at).
+__device__ __forceinline__ void bwd_localize(BwdArgs& a, int b) {
+  const SeqRows r = seq_localize(a.m, b);
+  if (a.m.cu_q) {
+    shift_rows<e16>(a.q, r.q0);
+    shift_rows<e16>(a.dout, r.q0);
+    shift_rows<e16>(a.dq, r.q0);
+    shift_rows<e16>(a.k, r.k0);
+    shift_rows<e16>(a.v, r.k0);
+    shift_rows<e16>(a.dk, r.k0);
+    shift_rows<e16>(a.dv, r.k0);
+  }
 }
 
 // Elementwise step of one 32x32 S/dP accumulator pair of the KV-outer kernel:
@@ -233,23 +242,22 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.m.n;
+  bwd_localize(a, b);
+  const int NQ = a.m.nq, NK = a.m.nk;
   const int kv0 = blk * C::BC;
+  if (kv0 >= NK) return;  // past this sequence's keys
   const int kvw = kv0 + 32 * w;
   const int key = kvw + c;  // this lane's key (column of S)
 
   // Query rows that can see at least one of the block's keys.
-  int q_lo = 0, q_hi = N;
-  if (a.m.causal) q_lo = max(q_lo, kv0);
-  if (a.m.wr >= 0) q_lo = max(q_lo, kv0 - a.m.wr);
-  if (a.m.wl >= 0) q_hi = min(q_hi, kv0 + C::BC + a.m.wl);
+  const int q_lo = max(0, kv0 - a.m.hi_off), q_hi = min(NQ, kv0 + C::BC + a.m.lo_off);
   const int it0 = q_lo / C::BR;
   const int it1 = q_lo < q_hi ? (q_hi + C::BR - 1) / C::BR : it0;
 
   // This wave's 32 keys: B operands of S = Q K^T and dP = dO V^T.
   e16x8 kreg[C::KT], vreg[C::KT];
   {
-    const bool ok = key < N;
+    const bool ok = key < NK;
     const e16* kp = at<e16>(a.k, b, h, ok ? key : 0);
     const e16* vp = at<e16>(a.v, b, h, ok ? key : 0);
 #pragma unroll
@@ -264,10 +272,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
     const int chunk = tid + x * C::NT;
     const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
     const int kr = kv0 + row;
-    store8(sK + row * C::LD + col, kr < N ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
+    store8(sK + row * C::LD + col, kr < NK ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
   }
 
-  const int64_t row_base = (int64_t)bh * N;
+  const int64_t row_base = (int64_t)bh * a.ln;
   e16x8 pq[C::LOADS], po[C::LOADS];
   float pl = 0.f, pd = 0.f;
 
@@ -278,7 +286,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int qr = q0 + row;
-      if (qr < N) {
+      if (qr < NQ) {
         pq[x] = load8(at<e16>(a.q, b, h, qr) + col);
         po[x] = load8(at<e16>(a.dout, b, h, qr) + col);
       } else {
@@ -288,8 +296,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
     }
     if (tid < C::BR) {
       const int qr = q0 + tid;
-      pl = qr < N ? a.lse[row_base + qr] * kLog2e : 0.f;
-      pd = qr < N ? a.delta[row_base + qr] : 0.f;
+      pl = qr < NQ ? a.lse[row_base + qr] * kLog2e : 0.f;
+      pd = qr < NQ ? a.delta[row_base + qr] : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -409,7 +417,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qr = q0 + 32 * (mt0 + mi) + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (qr < N) unsafeAtomicAdd(a.dq_acc + (row_base + qr) * D + 32 * nt + c, dq[mi][r]);
+          if (qr < NQ) unsafeAtomicAdd(a.dq_acc + (row_base + qr) * D + 32 * nt + c, dq[mi][r]);
         }
       }
     }
@@ -422,7 +430,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (kr < N) {
+      if (kr < NK) {
         at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dk_acc[n][r] * a.sm_scale);
         at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dv_acc[n][r]);
       }
@@ -466,15 +474,15 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   const int grp = w & 3, qh = w >> 2;
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.m.n;
+  bwd_localize(a, b);
+  const int NQ = a.m.nq, NK = a.m.nk;
   const int kv0 = blk * C::BC;
+  if (kv0 >= NK) return;  // past this sequence's keys
   const int kvw = kv0 + 32 * grp;
   const int key = kvw + c;
 
-  int q_lo = 0, q_hi = N;
-  if (a.m.causal) q_lo = max(q_lo, kv0);
-  if (a.m.wr >= 0) q_lo = max(q_lo, kv0 - a.m.wr);
-  if (a.m.wl >= 0) q_hi = min(q_hi, kv0 + C::BC + a.m.wl);
+  // Query rows that can see at least one of the block's keys.
+  const int q_lo = max(0, kv0 - a.m.hi_off), q_hi = min(NQ, kv0 + C::BC + a.m.lo_off);
   const int it0 = q_lo / C::BR;
   const int it1 = q_lo < q_hi ? (q_hi + C::BR - 1) / C::BR : it0;
 
@@ -484,11 +492,11 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     const int chunk = tid + x * C::NT;
     const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
     const int kr = kv0 + row;
-    store8(sK + row * C::LD + col, kr < N ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
-    store8(sV + row * C::LD + col, kr < N ? load8(at<e16>(a.v, b, h, kr) + col) : zero8());
+    store8(sK + row * C::LD + col, kr < NK ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
+    store8(sV + row * C::LD + col, kr < NK ? load8(at<e16>(a.v, b, h, kr) + col) : zero8());
   }
 
-  const int64_t row_base = (int64_t)bh * N;
+  const int64_t row_base = (int64_t)bh * a.ln;
   const char* q_head = (const char*)at<e16>(a.q, b, h, 0);
   const char* o_head = (const char*)at<e16>(a.dout, b, h, 0);
   const uint32_t q_rs = (uint32_t)a.q.sn * 2, o_rs = (uint32_t)a.dout.sn * 2;
@@ -500,13 +508,13 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int qr = min(q0 + row, N - 1);
+      const int qr = min(q0 + row, NQ - 1);  // rows past the end are masked: read a valid one
       pq[x] = load8((const e16*)row_addr(q_head, q_rs, qr) + col);
       po[x] = load8((const e16*)row_addr(o_head, o_rs, qr) + col);
     }
     if (tid < 2 * C::BR) {
       const int qr = q0 + (tid & (C::BR - 1));
-      pld = qr < N ? (tid < C::BR ? a.lse[row_base + qr] * kLog2e : a.delta[row_base + qr]) : 0.f;
+      pld = qr < NQ ? (tid < C::BR ? a.lse[row_base + qr] * kLog2e : a.delta[row_base + qr]) : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -582,12 +590,12 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     if (has_next) store_tile(buf ^ 1);
     lds_barrier();
   };
+  // Query blocks [itA, itB) see all 128 keys with no mask edge: the first
+  // query must reach the last key, the last query must still see the first.
   int itA = it1, itB = it1;
-  if (kv0 + C::BC <= N) {
-    int lo = 0, hi = N - C::BR;
-    if (a.m.causal) lo = max(lo, kv0 + C::BC - 1);
-    if (a.m.wr >= 0) lo = max(lo, kv0 + C::BC - 1 - a.m.wr);
-    if (a.m.wl >= 0) hi = min(hi, kv0 - C::BR + 1 + a.m.wl);
+  if (kv0 + C::BC <= NK) {
+    const int lo = max(0, kv0 + C::BC - 1 - a.m.hi_off);
+    const int hi = min(NQ - C::BR, kv0 - C::BR + 1 + a.m.lo_off);
     if (lo <= hi) {
       itA = min(max(it0, (lo + C::BR - 1) / C::BR), it1);
       itB = max(itA, min(it1, hi / C::BR + 1));
@@ -630,7 +638,7 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
         const float dkv = dk_acc[n][r] + xch[((grp * 2 * C::DT + n) * 16 + r) * 64 + lane];
         const float dvv = dv_acc[n][r] + xch[((grp * 2 * C::DT + C::DT + n) * 16 + r) * 64 + lane];
         const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (kr < N) {
+        if (kr < NK) {
           at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dkv * a.sm_scale);
           at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dvv);
         }
@@ -668,18 +676,20 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.m.n;
+  bwd_localize(a, b);
+  const int NQ = a.m.nq, NK = a.m.nk;
   // Longest first: with a causal mask the last query blocks see the most keys.
   const int qblk = a.m.causal ? gridDim.y - 1 - blk : blk;
   const int q0 = qblk * C::BQ;
+  if (q0 >= NQ) return;  // past this sequence's queries
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
-  const int64_t row_base = (int64_t)bh * N;
+  const int64_t row_base = (int64_t)bh * a.ln;
 
   // This wave's 32 queries: B operands of S^T = K Q^T and dP^T = V dO^T.
   e16x8 qreg[C::KT], oreg[C::KT];
   {
-    const bool ok = myq < N;
+    const bool ok = myq < NQ;
     const e16* qp = at<e16>(a.q, b, h, ok ? myq : 0);
     const e16* op = at<e16>(a.dout, b, h, ok ? myq : 0);
 #pragma unroll
@@ -688,13 +698,11 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
       oreg[t] = ok ? load8(op + 16 * t + 8 * g) : zero8();
     }
   }
-  const float l2 = myq < N ? a.lse[row_base + myq] * kLog2e : 0.f;
-  const float dd = myq < N ? a.delta[row_base + myq] : 0.f;
+  const float l2 = myq < NQ ? a.lse[row_base + myq] * kLog2e : 0.f;
+  const float dd = myq < NQ ? a.delta[row_base + myq] : 0.f;
 
-  int k_lo = 0, k_hi = N;
-  if (a.m.causal) k_hi = min(k_hi, q0 + C::BQ);
-  if (a.m.wl >= 0) k_lo = max(k_lo, q0 - a.m.wl);
-  if (a.m.wr >= 0) k_hi = min(k_hi, q0 + C::BQ + a.m.wr);
+  // Keys that at least one of the block's queries can see.
+  const int k_lo = max(0, q0 - a.m.lo_off), k_hi = min(NK, q0 + C::BQ + a.m.hi_off);
   const int jt0 = k_lo / C::BK;
   const int jt1 = k_lo < k_hi ? (k_hi + C::BK - 1) / C::BK : jt0;
 
@@ -708,7 +716,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int kr = min(k0 + row, N - 1);  // rows past the end are masked: read a valid one
+      const int kr = min(k0 + row, NK - 1);  // rows past the end are masked: read a valid one
       pk[x] = load8((const e16*)row_addr(k_head, k_rs, kr) + col);
       pv[x] = load8((const e16*)row_addr(v_head, v_rs, kr) + col);
     }
@@ -766,11 +774,9 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   // Key blocks [jtA, jtB) are seen by all 128 queries of the block with no
   // mask edge and no dropout.
   int jtA = jt1, jtB = jt1;
-  if (q0 + C::BQ <= N) {
-    int lo = 0, hi = N - C::BK;
-    if (a.m.causal) hi = min(hi, q0 - C::BK + 1);
-    if (a.m.wr >= 0) hi = min(hi, q0 + a.m.wr - C::BK + 1);
-    if (a.m.wl >= 0) lo = max(lo, q0 + C::BQ - 1 - a.m.wl);
+  if (q0 + C::BQ <= NQ) {
+    const int lo = max(0, q0 + C::BQ - 1 - a.m.lo_off);
+    const int hi = min(NK - C::BK, q0 + a.m.hi_off - C::BK + 1);
     if (lo <= hi) {
       jtA = min(max(jt0, (lo + C::BK - 1) / C::BK), jt1);
       jtB = max(jtA, min(jt1, hi / C::BK + 1));
@@ -862,7 +868,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qr = qw + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (qr < N) at<e16>(a.dq, b, h, qr)[32 * n + c] = (e16)(dq_acc[n][r] * a.sm_scale);
+      if (qr < NQ) at<e16>(a.dq, b, h, qr)[32 * n + c] = (e16)(dq_acc[n][r] * a.sm_scale);
     }
   }
 }
@@ -870,13 +876,13 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
   const int bh = a.B * a.H;
-  const dim3 grid_kv(bh, (a.m.n + KvCfg<D>::BC - 1) / KvCfg<D>::BC);
+  const dim3 grid_kv(bh, (a.m.nk + KvCfg<D>::BC - 1) / KvCfg<D>::BC);
   if (deterministic) {
     hipLaunchKernelGGL(a.m.dropout ? (dkdv_q2_kernel<D, true>) : (dkdv_q2_kernel<D, false>), grid_kv,
                        dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid_q(bh, (a.m.n + QCfg<D>::BQ - 1) / QCfg<D>::BQ);
+    const dim3 grid_q(bh, (a.m.nq + QCfg<D>::BQ - 1) / QCfg<D>::BQ);
     hipLaunchKernelGGL(a.m.dropout ? (dq_kernel<D, true>) : (dq_kernel<D, false>), grid_q, dim3(QCfg<D>::NT),
                        0, s, a);
   } else {

@@ -62,17 +62,52 @@ struct TensorView {
   int64_t sb, sh, sn;
 };
 
-// Mask and dropout flags of one call, in the form the kernels use.
+// Mask, sequence and dropout flags of one call, in the form the kernels use.
+// Query i of a sequence with nq queries and nk keys stands at key position
+// i + nk - nq (the last query aligns with the last key), so causal hides
+// j > i + nk - nq; that shift, causality and the window are folded into two
+// offsets.  The host fills the call-wide values (nq, nk = the longest
+// sequences); seq_localize turns them into those of one sequence.
 struct MaskArgs {
-  int n;              // sequence length
-  int causal;         // hide j > i
-  int wl, wr;         // window; -1 = unbounded
-  int lo_off, hi_off; // visible iff i - lo_off <= j <= i + hi_off (folds causal and window)
+  int nq, nk;         // query and key rows of the sequence
+  int causal;         // causal mask requested (used only to order work)
+  int lo_off, hi_off; // visible iff i - lo_off <= j <= i + hi_off
+  const int* cu_q;    // varlen: sequence b has rows [cu_q[b], cu_q[b+1]) of the packed
+  const int* cu_k;    //   query tensors and [cu_k[b], cu_k[b+1]) of the key ones; else null
   int dropout;        // 0/1
-  uint32_t keep_threshold;  // keep iff Philox word 0 >= threshold
+  uint32_t keep_threshold;  // keep iff the Philox word >= threshold
   float keep_scale;         // 1 / (1 - p)
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
 };
+
+// First packed row of one sequence's queries and keys.
+struct SeqRows {
+  int q0, k0;
+};
+
+// Specialise the call-wide mask to sequence b: its lengths (varlen: from the
+// offset arrays, clamped to [0, longest]) and the bottom-right shift
+// nk - nq folded into the offsets.  Returns the sequence's first rows.
+__device__ __forceinline__ SeqRows seq_localize(MaskArgs& m, int b) {
+  SeqRows r{0, 0};
+  if (m.cu_q) {
+    r.q0 = m.cu_q[b];
+    r.k0 = m.cu_k[b];
+    m.nq = min(max(m.cu_q[b + 1] - r.q0, 0), m.nq);
+    m.nk = min(max(m.cu_k[b + 1] - r.k0, 0), m.nk);
+  }
+  const int shift = m.nk - m.nq;
+  m.lo_off -= shift;
+  m.hi_off += shift;
+  return r;
+}
+
+// Move a tensor view to the first packed row of a sequence (varlen; the
+// host zeroes the batch stride there).
+template <typename T>
+__device__ __forceinline__ void shift_rows(TensorView& t, int rows) {
+  t.ptr = (T*)t.ptr + (int64_t)rows * t.sn;
+}
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -117,10 +152,10 @@ __device__ __forceinline__ e16x8 tr_operand(const e16* tile, int ld, int row_lo,
 __host__ __device__ constexpr int lds_stride(int cols) { return cols == 128 ? 152 : 104; }
 
 // valid(i, j): key j visible to query i ("Lecture 7", "Mask behaviour").
-// Causal and window bounds are folded into two offsets on the host, so the
+// Causal, window and alignment bounds are folded into two offsets, so the
 // test is branch-free.
 __device__ __forceinline__ bool visible(const MaskArgs& m, int i, int j) {
-  return (i < m.n) & (j < m.n) & (j >= i - m.lo_off) & (j <= i + m.hi_off);
+  return (i < m.nq) & (j < m.nk) & (j >= i - m.lo_off) & (j <= i + m.hi_off);
 }
 
 // Barrier that orders LDS accesses only: global stores and atomics in flight

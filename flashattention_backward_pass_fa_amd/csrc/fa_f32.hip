@@ -14,30 +14,49 @@
 namespace fa {
 namespace {
 
-// Visible key range [lo, hi) of query row i.
+// Visible key range [lo, hi) of query row i (empty when hi <= lo).
 __device__ __forceinline__ void key_range(const MaskArgs& m, int i, int& lo, int& hi) {
-  lo = 0;
-  hi = m.n;
-  if (m.causal) hi = min(hi, i + 1);
-  if (m.wl >= 0) lo = max(lo, i - m.wl);
-  if (m.wr >= 0) hi = min(hi, i + m.wr + 1);
+  lo = max(0, i - m.lo_off);
+  hi = min(m.nk, i + m.hi_off + 1);
 }
 
 // Query range [lo, hi) that sees key row j.
 __device__ __forceinline__ void query_range(const MaskArgs& m, int j, int& lo, int& hi) {
-  lo = 0;
-  hi = m.n;
-  if (m.causal) lo = max(lo, j);
-  if (m.wr >= 0) lo = max(lo, j - m.wr);
-  if (m.wl >= 0) hi = min(hi, j + m.wl + 1);
+  lo = max(0, j - m.hi_off);
+  hi = min(m.nq, j + m.lo_off + 1);
+}
+
+// Specialise a call to sequence b: lengths, mask offsets, packed rows.
+__device__ __forceinline__ void localize(FwdArgs& a, int b) {
+  const SeqRows r = seq_localize(a.m, b);
+  if (a.m.cu_q) {
+    shift_rows<float>(a.q, r.q0);
+    shift_rows<float>(a.o, r.q0);
+    shift_rows<float>(a.k, r.k0);
+    shift_rows<float>(a.v, r.k0);
+  }
+}
+
+__device__ __forceinline__ void localize(BwdArgs& a, int b) {
+  const SeqRows r = seq_localize(a.m, b);
+  if (a.m.cu_q) {
+    shift_rows<float>(a.q, r.q0);
+    shift_rows<float>(a.dout, r.q0);
+    shift_rows<float>(a.dq, r.q0);
+    shift_rows<float>(a.k, r.k0);
+    shift_rows<float>(a.v, r.k0);
+    shift_rows<float>(a.dk, r.k0);
+    shift_rows<float>(a.dv, r.k0);
+  }
 }
 
 template <int DM>
 __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
   const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
+  localize(a, b);
   const int i = blockIdx.y * 64 + threadIdx.x;
-  const int N = a.m.n, d = a.d;
-  if (i >= N) return;
+  const int d = a.d;
+  if (i >= a.m.nq) return;
   const float scale = a.sm_scale;
   float q[DM], o[DM];
   const float* qp = at<float>(a.q, b, h, i);
@@ -68,21 +87,23 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
       if (c < d) o[c] = fmaf(pd, vp[c], o[c] * alpha);
     m_run = m_new;
   }
+  // a row that sees no key has an empty sum: O = 0 and L = log 0 = -inf
   float* op = at<float>(a.o, b, h, i);
-  const float inv = 1.f / l_run;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
   for (int c = 0; c < DM; ++c)
     if (c < d) op[c] = o[c] * inv;
-  a.lse[(int64_t)bh * N + i] = m_run + logf(l_run);
+  a.lse[(int64_t)bh * a.ln + i] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 
 template <int DM>
 __global__ void __launch_bounds__(64) dkdv_f32_kernel(BwdArgs a) {
   const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
+  localize(a, b);
   const int j = blockIdx.y * 64 + threadIdx.x;
-  const int N = a.m.n, d = a.d;
-  if (j >= N) return;
-  const int64_t row_base = (int64_t)bh * N;
+  const int d = a.d;
+  if (j >= a.m.nk) return;
+  const int64_t row_base = (int64_t)bh * a.ln;
   float kj[DM], vj[DM], dk[DM], dv[DM];
   const float* kp = at<float>(a.k, b, h, j);
   const float* vp = at<float>(a.v, b, h, j);
@@ -133,10 +154,11 @@ __global__ void __launch_bounds__(64) dkdv_f32_kernel(BwdArgs a) {
 template <int DM>
 __global__ void __launch_bounds__(64) dq_f32_kernel(BwdArgs a) {
   const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
+  localize(a, b);
   const int i = blockIdx.y * 64 + threadIdx.x;
-  const int N = a.m.n, d = a.d;
-  if (i >= N) return;
-  const int64_t row_base = (int64_t)bh * N;
+  const int d = a.d;
+  if (i >= a.m.nq) return;
+  const int64_t row_base = (int64_t)bh * a.ln;
   float qi[DM], gi[DM], dq[DM];
   const float* qp = at<float>(a.q, b, h, i);
   const float* gp = at<float>(a.dout, b, h, i);
@@ -174,17 +196,16 @@ __global__ void __launch_bounds__(64) dq_f32_kernel(BwdArgs a) {
 
 template <int DM>
 hipError_t launch_fwd_dm(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_f32_kernel<DM>, dim3(a.B * a.H, (a.m.n + 63) / 64), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(fwd_f32_kernel<DM>, dim3(a.B * a.H, (a.m.nq + 63) / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DM>
 hipError_t launch_bwd_dm(const BwdArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.H, (a.m.n + 63) / 64);
-  hipLaunchKernelGGL(dkdv_f32_kernel<DM>, grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL(dkdv_f32_kernel<DM>, dim3(a.B * a.H, (a.m.nk + 63) / 64), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dq_f32_kernel<DM>, grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL(dq_f32_kernel<DM>, dim3(a.B * a.H, (a.m.nq + 63) / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -53,24 +53,34 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), c = lane & 31, g = lane >> 5;
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.m.n;
+  {
+    const SeqRows r = seq_localize(a.m, b);
+    if (a.m.cu_q) {
+      shift_rows<e16>(a.q, r.q0);
+      shift_rows<e16>(a.o, r.q0);
+      shift_rows<e16>(a.k, r.k0);
+      shift_rows<e16>(a.v, r.k0);
+    }
+  }
+  const int NQ = a.m.nq, NK = a.m.nk;
   // Longest first: with a causal mask the last query blocks see the most keys.
   const int q0 = (a.m.causal ? gridDim.y - 1 - blk : blk) * C::BQ;
+  if (q0 >= NQ) return;  // past this sequence's queries
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
 
   e16x8 qreg[C::KT];
   {
-    const bool ok = myq < N;
+    const bool ok = myq < NQ;
     const e16* qp = at<e16>(a.q, b, h, ok ? myq : 0);
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) qreg[t] = ok ? load8(qp + 16 * t + 8 * g) : zero8();
   }
 
-  int k_lo = 0, k_hi = N;
-  if (a.m.causal) k_hi = min(k_hi, q0 + C::BQ);
-  if (a.m.wl >= 0) k_lo = max(k_lo, q0 - a.m.wl);
-  if (a.m.wr >= 0) k_hi = min(k_hi, q0 + C::BQ + a.m.wr);
+  // Keys that at least one of the block's queries can see (workgroup-uniform;
+  // saying so keeps the loop bounds in scalar registers).
+  const int k_lo = __builtin_amdgcn_readfirstlane(max(0, q0 - a.m.lo_off));
+  const int k_hi = __builtin_amdgcn_readfirstlane(min(NK, q0 + C::BQ + a.m.hi_off));
   const int jt0 = k_lo / C::BK;
   const int jt1 = k_lo < k_hi ? (k_hi + C::BK - 1) / C::BK : jt0;
 
@@ -82,7 +92,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int kr = k0 + row;
-      if (kr < N) {
+      if (kr < NK) {
         pk[x] = load8(at<e16>(a.k, b, h, kr) + col);
         pv[x] = load8(at<e16>(a.v, b, h, kr) + col);
       } else {
@@ -189,14 +199,12 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     __syncthreads();
   };
   // Key blocks [jtA, jtB) are seen by all 128 queries of the block with no
-  // mask edge: causality and the right window bound k0 from above, the left
-  // window from below.
+  // mask edge: the first query bounds k0 from above (causality, right
+  // window), the last query from below (left window).
   int jtA = jt1, jtB = jt1;
-  if (q0 + C::BQ <= N) {
-    int lo = 0, hi = N - C::BK;
-    if (a.m.causal) hi = min(hi, q0 - C::BK + 1);
-    if (a.m.wr >= 0) hi = min(hi, q0 + a.m.wr - C::BK + 1);
-    if (a.m.wl >= 0) lo = max(lo, q0 + C::BQ - 1 - a.m.wl);
+  if (q0 + C::BQ <= NQ) {
+    const int lo = max(0, q0 + C::BQ - 1 - a.m.lo_off);
+    const int hi = min(NK - C::BK, q0 + a.m.hi_off - C::BK + 1);
     if (lo <= hi) {
       jtA = min(max(jt0, (lo + C::BK - 1) / C::BK), jt1);
       jtB = max(jtA, min(jt1, hi / C::BK + 1));
@@ -210,8 +218,10 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   for (; jt < jt1; ++jt) step(jt, general);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (myq < N) {
-    const float inv = 1.0f / l_tot;
+  if (myq < NQ) {
+    // a row that sees no key (possible when nq > nk, or through a window)
+    // has an empty sum: O = 0 and L = log 0 = -inf
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     e16* op = at<e16>(a.o, b, h, myq);
 #pragma unroll
     for (int n = 0; n < C::DT; ++n) {
@@ -222,14 +232,14 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
         *(e16x4*)(op + 32 * n + 8 * rr + 4 * g) = v4;
       }
     }
-    if (g == 0) a.lse[(int64_t)bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (g == 0) a.lse[(int64_t)bh * a.ln + myq] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
 }  // namespace
 
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.H, (a.m.n + 127) / 128);
+  const dim3 grid(a.B * a.H, (a.m.nq + 127) / 128);
   if (a.d == 128)
     hipLaunchKernelGGL(a.m.dropout ? (fwd_kernel<128, true>) : (fwd_kernel<128, false>), grid, dim3(256), 0, s, a);
   else

@@ -11,8 +11,9 @@ namespace fa {
 // Arguments of the forward kernels.
 struct FwdArgs {
   TensorView q, k, v, o;
-  float* lse;          // [B, H, N] fp32
+  float* lse;          // [B, H, ln] fp32
   int B, H, d;
+  int ln;              // rows per head of L (the longest query sequence)
   float sm_scale;
   float scale_log2;    // sm_scale * log2(e)
   MaskArgs m;
@@ -21,10 +22,11 @@ struct FwdArgs {
 // Arguments of the backward kernels.
 struct BwdArgs {
   TensorView q, k, v, dout, dq, dk, dv;
-  const float* lse;    // [B, H, N] fp32, natural log
-  const float* delta;  // [B, H, N] fp32
-  float* dq_acc;       // [B, H, N, d] fp32 (atomic mode)
+  const float* lse;    // [B, H, ln] fp32, natural log
+  const float* delta;  // [B, H, ln] fp32
+  float* dq_acc;       // [B, H, ln, d] fp32 (atomic mode)
   int B, H, d;
+  int ln;              // rows per head of L, D and dq_acc (the longest query sequence)
   float sm_scale;
   float scale_log2;
   MaskArgs m;
@@ -33,9 +35,10 @@ struct BwdArgs {
 // Arguments of the pre-pass (D) and the dQ conversion.
 struct PrepArgs {
   TensorView o, dout, dq;
-  float* delta;
-  float* dq_acc;
-  int B, H, N, d;
+  float* delta;        // [B, H, N] fp32
+  float* dq_acc;       // [B, H, N, d] fp32
+  const int* cu_q;     // varlen: sequence b has packed rows [cu_q[b], cu_q[b+1]); else null
+  int B, H, N, d;      // N: rows per head of delta and dq_acc (the longest query sequence)
   int dtype;           // element type of o/dout/dq: 0 fp32, 1 bf16, 2 fp16 (fa_dtype)
   float sm_scale;
 };

@@ -47,6 +47,17 @@ __device__ __forceinline__ void store_scaled8(T* dst, f32x4 x0, f32x4 x1, float 
   *(T8*)dst = y;
 }
 
+// zero one row of the fp32 dQ accumulator (atomic mode), 16 lanes per row
+__device__ __forceinline__ void zero_acc_row(const PrepArgs& a, int64_t row, int sub) {
+  if (!a.dq_acc) return;
+  float* zrow = a.dq_acc + row * a.d;
+  if ((a.d & 3) == 0) {
+    for (int c4 = sub; c4 * 4 < a.d; c4 += 16) ((f32x4*)zrow)[c4] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    for (int c = sub; c < a.d; c += 16) zrow[c] = 0.f;
+  }
+}
+
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
   const int sub = threadIdx.x & 15;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
@@ -55,7 +66,16 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
        row += (int64_t)gridDim.x * kRowsPerBlock) {
     const int b = (int)(row / HN);
     const int rem = (int)(row - b * HN);
-    const int h = rem / a.N, n = rem - h * a.N;
+    const int h = rem / a.N;
+    int n = rem - h * a.N;
+    if (a.cu_q) {  // varlen: rows past sequence b's length hold no query
+      const int q0 = a.cu_q[b];
+      if (n >= a.cu_q[b + 1] - q0) {
+        zero_acc_row(a, row, sub);
+        continue;
+      }
+      n += q0;
+    }
     float acc = 0.f;
     if (a.dtype == 1) {
       acc = row_dot16<bf16, bf16x8>(a.o, a.dout, b, h, n, a.d, sub);
@@ -69,14 +89,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
     if (sub == 0) a.delta[row] = acc;
-    if (a.dq_acc) {
-      float* zrow = a.dq_acc + row * a.d;
-      if ((a.d & 3) == 0) {
-        for (int c4 = sub; c4 * 4 < a.d; c4 += 16) ((f32x4*)zrow)[c4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else {
-        for (int c = sub; c < a.d; c += 16) zrow[c] = 0.f;
-      }
-    }
+    zero_acc_row(a, row, sub);
   }
 }
 
@@ -91,7 +104,13 @@ __global__ void __launch_bounds__(256) dq_convert_kernel(PrepArgs a) {
     const int c0 = (int)(t - row * per_row) * 8;
     const int b = (int)(row / HN);
     const int rem = (int)(row - b * HN);
-    const int h = rem / a.N, n = rem - h * a.N;
+    const int h = rem / a.N;
+    int n = rem - h * a.N;
+    if (a.cu_q) {  // varlen: rows past sequence b's length hold no query
+      const int q0 = a.cu_q[b];
+      if (n >= a.cu_q[b + 1] - q0) continue;
+      n += q0;
+    }
     const f32x4* src = (const f32x4*)(a.dq_acc + row * a.d + c0);
     const f32x4 x0 = src[0], x1 = src[1];
     if (a.dtype == 2)
@@ -104,7 +123,7 @@ __global__ void __launch_bounds__(256) dq_convert_kernel(PrepArgs a) {
 __global__ void __launch_bounds__(256) mask_kernel(MaskArgs m, int b, int h, uint8_t* out) {
   const int i = blockIdx.x;
   const int j = blockIdx.y * 256 + threadIdx.x;
-  if (j < m.n) out[(int64_t)i * m.n + j] = dropout_keep(m, b, h, i, j) ? 1 : 0;
+  if (j < m.nk) out[(int64_t)i * m.nk + j] = dropout_keep(m, b, h, i, j) ? 1 : 0;
 }
 
 int grid_for(int64_t work_items, int per_block) {
@@ -130,7 +149,7 @@ hipError_t launch_dq_convert(const PrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dropout_mask(const MaskArgs& m, int b, int h, uint8_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(mask_kernel, dim3(m.n, (m.n + 255) / 256), dim3(256), 0, s, m, b, h, out);
+  hipLaunchKernelGGL(mask_kernel, dim3(m.nq, (m.nk + 255) / 256), dim3(256), 0, s, m, b, h, out);
   return hipGetLastError();
 }
 

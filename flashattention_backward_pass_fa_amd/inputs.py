@@ -77,16 +77,20 @@ def bf16_bits_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def make_tensors(shape, dtype, seed, names=("q", "k", "v", "do")):
+def make_tensors(shape, dtype, seed, names=("q", "k", "v", "do"), shapes=None):
     """Draw the named tensors in order from PCG64(seed).
 
-    Returns {name: fp32 array of the exact stored values} and, for bf16 and
-    fp16, {name + "_bits": uint16 bit patterns} for upload to the device.
+    shapes: optional {name: shape} for tensors whose shape differs from
+    `shape` (keys and values of a problem with Nk != Nq, packed varlen
+    tensors).  Returns {name: fp32 array of the exact stored values} and,
+    for bf16 and fp16, {name + "_bits": uint16 bit patterns} for upload to
+    the device.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {}
     for name in names:
-        x = rng.standard_normal(shape, dtype=np.float64).astype(np.float32)
+        shp = shapes.get(name, shape) if shapes else shape
+        x = rng.standard_normal(shp, dtype=np.float64).astype(np.float32)
         if dtype == "bf16":
             bits = round_to_bf16_bits(x)
             out[name + "_bits"] = bits
@@ -100,6 +104,30 @@ def make_tensors(shape, dtype, seed, names=("q", "k", "v", "do")):
         else:
             raise ValueError(f"unsupported dtype {dtype!r}")
     return out
+
+
+def varlen_lengths(count, lo, hi, seed):
+    """`count` sequence lengths drawn uniformly from [lo, hi] with PCG64(seed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [int(x) for x in rng.integers(lo, hi + 1, size=count)]
+
+
+def pack_lengths(total, lo, hi, seed):
+    """Lengths in [lo, hi] drawn with PCG64(seed) until they fill `total`
+    tokens; the last one is cut to fit (a packed batch of a fixed token
+    count, as a training step packs documents of mixed length)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out, used = [], 0
+    while used < total:
+        n = min(int(rng.integers(lo, hi + 1)), total - used)
+        out.append(n)
+        used += n
+    return out
+
+
+def cumulative(lengths):
+    """Offsets [0, l0, l0 + l1, ...] of packed sequences (int32)."""
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
 
 
 def make_workload_inputs(w):

@@ -14,17 +14,23 @@
  *   forward left behind" (O and L_i = m_i + log l_i), "The gradients, and the
  *   one scalar that makes them local" (D), "The loop structure" (KV-outer
  *   loop; dQ by atomics or by a separate Q-outer kernel).
+ *   Lecture 7's section on the FA test suite lists variable-length batches
+ *   among the features a harness covers; the pages define no convention for
+ *   them, so the one below is this library's (see fa_params).
  *
  * Conventions shared by every entry point
  *   - Tensors Q, K, V, O, dO, dQ, dK, dV are described by fa_tensor: a device
  *     pointer and element strides for the batch, head and sequence axes; the
  *     head-dim axis has stride 1.  [B,H,N,d] contiguous and [B,N,H,d] are
- *     both expressible.  bf16 and fp16 tensors need a 16-byte aligned
+ *     both expressible.  Q, O, dO, dQ have N = seqlen rows per head and
+ *     K, V, dK, dV have N = seqlen_k (or, in varlen mode, the packed rows
+ *     of fa_params).  bf16 and fp16 tensors need a 16-byte aligned
  *     pointer and strides that are multiples of 8 elements, and fit each
  *     row stride in 32 bits of bytes; fp32 tensors need 4-byte alignment.
- *   - L (lse), D (delta) are fp32, [B,H,N] contiguous.  L is the natural log
- *     of sum_j exp(S_ij) over the visible keys of row i, with
- *     S = sm_scale * Q K^T.
+ *   - L (lse), D (delta) are fp32, [B,H,seqlen] contiguous.  L is the natural
+ *     log of sum_j exp(S_ij) over the visible keys of row i, with
+ *     S = sm_scale * Q K^T; a row that sees no key has L = -inf, O = 0 and
+ *     dQ = 0.
  *   - Ownership: the caller allocates every buffer (device memory) and keeps
  *     it alive until the work on `stream` completes.  The library allocates
  *     no device memory, keeps no pointer after a call returns and holds no
@@ -50,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum fa_status {
   FA_SUCCESS = 0,
@@ -79,32 +85,54 @@ typedef struct fa_tensor {
 /* Flags and sizes of one attention call.
  *   dtype         FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16
  *   batch, heads  B, H >= 1
- *   seqlen        1 <= N <= 2^21 (queries and keys have the same length);
- *                 B * H * ceil(N / 64) must stay below 2^31
+ *   seqlen        Nq, queries per sequence, 1 <= Nq <= 2^21
+ *   seqlen_k      Nk, keys per sequence, 1 <= Nk <= 2^21;
+ *                 B * H * ceil(max(Nq, Nk) / 64) must stay below 2^31
  *   head_dim      d: bf16 and fp16 support 64 and 128; fp32 supports 1..128
  *   sm_scale      S = sm_scale * Q K^T (the pages use 1/sqrt(d)); any finite
  *                 value, 0 included
- *   causal        non-zero: key j is hidden from query i when j > i
- *   window_left   -1 = unbounded, else keys j >= i - window_left only
- *   window_right  -1 = unbounded, else keys j <= i + window_right only
- *                 (with causal and windows >= 0, key i is always visible, so
- *                 no row is ever empty)
+ *   Masks align the last query with the last key: query i stands at key
+ *   position i' = i + Nk - Nq (i' = i when Nq = Nk).
+ *   causal        non-zero: key j is hidden from query i when j > i'
+ *   window_left   -1 = unbounded, else keys j >= i' - window_left only
+ *   window_right  -1 = unbounded, else keys j <= i' + window_right only
+ *                 (with Nq = Nk and windows >= 0 key i is always visible;
+ *                 with Nq > Nk, or a window that misses [0, Nk), a row can
+ *                 see no key)
  *   dropout_p     probability of dropping an attention weight, in [0, 1);
- *                 kept weights are scaled by 1/(1 - p).  Requires B, H, N
- *                 <= 65536 when p > 0.
+ *                 kept weights are scaled by 1/(1 - p).  Requires B, H, Nq,
+ *                 Nk <= 65536 when p > 0.
  *   seed, offset  Philox4x32-10 stream of the dropout mask: key = seed,
  *                 one block per four keys j4 = j - j % 4, counter =
  *                 (offset, (i << 16) | j4, (b << 16) | h); weight
- *                 (b, h, i, j) is kept iff word j % 4 >= ceil(p * 2^32).
+ *                 (b, h, i, j) is kept iff word j % 4 >= ceil(p * 2^32);
+ *                 i and j count from the start of the sequence.
  *   deterministic non-zero: dQ by a separate Q-outer kernel, bit-identical
  *                 run to run; zero: for bf16/fp16, dQ by fp32 atomics into
  *                 a workspace (fp32 computes dQ without atomics either way).
+ *   cu_seqlens_q, cu_seqlens_k
+ *                 NULL (both): every sequence has Nq queries and Nk keys at
+ *                 tensor rows 0.. of its batch index.  Non-NULL (both):
+ *                 varlen mode, device arrays of B + 1 int32 each; sequence b
+ *                 has queries at packed rows [cu_seqlens_q[b],
+ *                 cu_seqlens_q[b+1]) and keys at [cu_seqlens_k[b],
+ *                 cu_seqlens_k[b+1]) of the tensors (row r of head h at
+ *                 ptr + h*stride_h + r*stride_n; stride_b is ignored), and
+ *                 seqlen / seqlen_k are the longest lengths.  Lengths are
+ *                 clamped to [0, seqlen] / [0, seqlen_k] and each sequence
+ *                 aligns its own last query and key.  L, D and the dQ
+ *                 workspace keep the [B,H,seqlen] layout: entries past a
+ *                 sequence's length are not written.  The caller keeps the
+ *                 arrays (and every packed row they name) valid until the
+ *                 work completes; they cannot be checked without a copy to
+ *                 the host.
  */
 typedef struct fa_params {
   int32_t dtype;
   int32_t batch;
   int32_t heads;
   int32_t seqlen;
+  int32_t seqlen_k;
   int32_t head_dim;
   float sm_scale;
   int32_t causal;
@@ -114,6 +142,8 @@ typedef struct fa_params {
   double dropout_p;
   uint64_t seed;
   uint64_t offset;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
 } fa_params;
 
 /* FA_ABI_VERSION of the built library. */
@@ -142,9 +172,9 @@ fa_status fa_fwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
 fa_status fa_bwd_preprocess(const fa_params* params, fa_tensor o, fa_tensor dout,
                             float* delta, float* dq_acc, void* stream);
 
-/* Bytes of fp32 workspace fa_bwd needs: 4*B*H*N*d for bf16/fp16 with
- * deterministic == 0 (the dQ accumulator, [B,H,N,d] contiguous), else 0
- * (also 0 when params are invalid). */
+/* Bytes of fp32 workspace fa_bwd needs: 4*B*H*seqlen*d for bf16/fp16 with
+ * deterministic == 0 (the dQ accumulator, [B,H,seqlen,d] contiguous), else
+ * 0 (also 0 when params are invalid). */
 size_t fa_bwd_workspace_bytes(const fa_params* params);
 
 /* Backward: dQ, dK, dV in the input dtype ("Lecture 7", "The math";
@@ -157,10 +187,11 @@ fa_status fa_bwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc,
                  void* stream);
 
-/* Test aid, O(N^2) by design: writes the N x N keep mask Z (1 = kept, 0 =
- * dropped; row i = query, column j = key) of head (b, h) to device memory
- * `mask` (uint8, row-major), using the same device function as the kernels.
- * Masked-out (invisible) pairs are still written with their Philox value. */
+/* Test aid, O(Nq Nk) by design: writes the Nq x Nk keep mask Z (1 = kept,
+ * 0 = dropped; row i = query, column j = key) of head (b, h) to device
+ * memory `mask` (uint8, row-major), using the same device function as the
+ * kernels.  Masked-out (invisible) pairs are still written with their
+ * Philox value; varlen offsets play no part (b is the sequence index). */
 fa_status fa_debug_dropout_mask(const fa_params* params, int32_t b, int32_t h,
                                 uint8_t* mask, void* stream);
 

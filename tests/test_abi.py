@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert fa.fa_abi_version() == fa.ABI_VERSION == 1
+    assert fa.fa_abi_version() == fa.ABI_VERSION == 2
     for code in range(6):
         s = fa.fa_status_string(code)
         assert isinstance(s, str) and s
@@ -51,18 +51,18 @@ def test_abi_version_and_status_strings(lib):
 
 def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "layout.c"
+    fields = ("seqlen", "seqlen_k", "head_dim", "sm_scale", "deterministic", "dropout_p", "seed",
+              "offset", "cu_seqlens_q", "cu_seqlens_k")
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fa.h"\n'
-                   'int main(){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(fa_params),'
-                   ' offsetof(fa_params, sm_scale), offsetof(fa_params, deterministic),'
-                   ' offsetof(fa_params, dropout_p), offsetof(fa_params, seed),'
-                   ' offsetof(fa_params, offset), sizeof(fa_tensor)); return 0;}\n')
+                   'int main(){printf("%zu %zu'
+                   + " %zu" * len(fields) + '\\n", sizeof(fa_params), sizeof(fa_tensor)'
+                   + "".join(f", offsetof(fa_params, {f})" for f in fields) + '); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
     P = fa.FaParams
-    assert got == [ctypes.sizeof(P), P.sm_scale.offset, P.deterministic.offset,
-                   P.dropout_p.offset, P.seed.offset, P.offset.offset, ctypes.sizeof(fa.FaTensor)]
+    assert got == [ctypes.sizeof(P), ctypes.sizeof(fa.FaTensor)] + [getattr(P, f).offset for f in fields]
 
 
 # ------------------------------------------------ validation (no HIP call)
@@ -97,6 +97,14 @@ VOID = ctypes.c_void_p
     (dict(shape=(1, 1, 70000, 64), dropout_p=0.1), 2),   # dropout counter holds 16-bit indices
     (dict(shape=(1, 1, (1 << 21) + 1, 64)), 2),           # longest sequence is 2^21
     (dict(shape=(1 << 16, 1 << 12, 1 << 10, 64)), 2),     # workgroup count past 2^31
+    (dict(seqlen_k=0), 1),
+    (dict(seqlen_k=(1 << 21) + 1), 2),                      # keys too
+    (dict(shape=(1 << 16, 1 << 12, 64, 64), seqlen_k=1 << 10), 2),  # the longer length counts
+    (dict(seqlen_k=70000, dropout_p=0.1), 2),
+    (dict(cu_seqlens_q=0x700000), 1),                       # varlen needs both offset arrays
+    (dict(cu_seqlens_k=0x700000), 1),
+    (dict(cu_seqlens_q=0x700002, cu_seqlens_k=0x700000), 3),  # int32 alignment
+    (dict(cu_seqlens_q=0x700000, cu_seqlens_k=0x700001), 3),
 ])
 def test_invalid_params_rejected(lib, mutate, status):
     p = _params(**mutate)
@@ -147,6 +155,25 @@ def test_workspace_bytes(lib):
 def _no_gpu():
     import torch
     return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device path; needs a host without a GPU")
+def test_varlen_ignores_the_batch_stride(lib):
+    # a batch stride that is not a multiple of 8 is misaligned in fixed-length
+    # mode but ignored in varlen mode (validation passes; no device -> 5)
+    odd = fa.FaTensor(0x100000, 12, 64, 256)
+    others = [_t(0x100000 * (i + 2)) for i in range(6)]
+    lse, delta = VOID(0x900000), VOID(0xA00000)
+    fixed = _params(deterministic=True)
+    assert fa.fa_bwd(fixed, odd, *others[:3], lse, delta, *others[3:], VOID(0), VOID(0)) == 3
+    var = _params(deterministic=True, cu_seqlens_q=0x700000, cu_seqlens_k=0x710000)
+    assert fa.fa_bwd(var, odd, *others[:3], lse, delta, *others[3:], VOID(0), VOID(0)) == 5
+
+
+def test_workspace_bytes_follow_the_query_length(lib):
+    # the dQ accumulator is [B, H, seqlen, d] whatever the key length
+    p = _params(shape=(2, 3, 100, 128), seqlen_k=37)
+    assert fa.fa_bwd_workspace_bytes(p) == 4 * 2 * 3 * 100 * 128
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="checks the no-device path; needs a host without a GPU")

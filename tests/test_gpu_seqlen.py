@@ -1,0 +1,144 @@
+"""GPU parity with unequal query/key lengths (last query aligned with the last
+key) and with packed variable-length batches, through the C ABI, against the
+fp64 oracle, element by element, in both dQ modes."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from flashattention_backward_pass_fa_amd import binding as fa
+from flashattention_backward_pass_fa_amd.inputs import cumulative, make_tensors
+from tests.gpu_cases import assert_close, to_device, to_host, zero_floor
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(d, causal, window, p, sm_scale=None):
+    return oracle.Spec(sm_scale=1.0 / math.sqrt(d) if sm_scale is None else sm_scale,
+                       causal=causal, window_left=window[0], window_right=window[1],
+                       dropout_p=p, seed=0x5EED, offset=3)
+
+
+def _kw(spec):
+    return dict(sm_scale=spec.sm_scale, causal=spec.causal,
+                window=(spec.window_left, spec.window_right), dropout_p=spec.dropout_p,
+                seed=spec.seed, offset=spec.offset)
+
+
+def _upload(host, dtype, names=("q", "k", "v", "do")):
+    return {n: to_device(host[n], host.get(n + "_bits"), dtype) for n in names}
+
+
+def _check_lse(got, want):
+    got, want = np.asarray(got), np.asarray(want)
+    assert np.array_equal(np.isneginf(got), np.isneginf(want)), "rows without keys must have L = -inf"
+    live = np.isfinite(want)
+    if live.any():
+        err = float(np.abs(got[live] - want[live]).max())
+        assert err <= 1e-3, f"lse: max|err| {err:.3e}"
+
+
+# (B, H, Nq, Nk, d, dtype, causal, window, p)
+UNEQUAL = [
+    (1, 2, 77, 300, 64, "bf16", True, (-1, -1), 0.0),
+    (1, 2, 300, 77, 128, "bf16", True, (-1, -1), 0.0),     # 223 rows see no key
+    (2, 2, 513, 1000, 128, "bf16", False, (100, 37), 0.0),
+    (1, 2, 1000, 130, 64, "bf16", False, (-1, 0), 0.0),
+    (1, 2, 200, 600, 128, "bf16", True, (-1, -1), 0.1),
+    (1, 1, 1, 700, 64, "bf16", True, (-1, -1), 0.0),       # one query over a long context
+    (1, 2, 640, 256, 128, "f16", True, (64, -1), 0.0),
+    (1, 2, 50, 130, 40, "f32", True, (-1, -1), 0.0),
+    (1, 1, 130, 50, 64, "f32", False, (10, 5), 0.2),
+]
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk,d,dtype,causal,window,p", UNEQUAL)
+def test_unequal_lengths(B, H, Nq, Nk, d, dtype, causal, window, p, deterministic):
+    print(f"\n[gpu] unequal B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} "
+          f"window={window} p={p} det={deterministic}", flush=True)
+    spec = _spec(d, causal, window, p)
+    host = make_tensors((B, H, Nq, d), dtype, 17 + Nq + Nk,
+                        shapes={"k": (B, H, Nk, d), "v": (B, H, Nk, d)})
+    dev = _upload(host, dtype)
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], **_kw(spec))
+    dq, dk, dv, delta = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse,
+                                    deterministic=deterministic, **_kw(spec))
+    import torch
+    torch.cuda.synchronize()
+    ref = oracle.backward(host["q"], host["k"], host["v"], host["do"], spec)
+    mags = {n: float(np.abs(host[n]).max()) for n in ("q", "k", "v", "do")}
+    for name, got in (("o", o), ("delta", delta), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(name, to_host(got), ref[name], dtype, zero_floor(name, dtype, d, spec.sm_scale, mags))
+    _check_lse(to_host(lse), ref["lse"])
+    if causal and Nq > Nk and window[0] < 0:
+        empty = Nq - Nk
+        assert np.all(to_host(o)[:, :, :empty] == 0) and np.all(to_host(dq)[:, :, :empty] == 0)
+
+
+# (lengths_q, lengths_k, H, d, dtype, causal, window, p)
+VARLEN = [
+    ([300, 0, 77, 1, 1000, 129], [300, 5, 77, 1, 1000, 129], 2, 128, "bf16", True, (-1, -1), 0.0),
+    ([513, 64, 200], [100, 700, 200], 2, 64, "bf16", True, (-1, -1), 0.0),
+    ([257, 640, 33, 90], [257, 640, 0, 90], 3, 128, "bf16", False, (100, 37), 0.0),
+    ([400, 129, 7], [400, 129, 7], 2, 64, "bf16", True, (-1, -1), 0.2),
+    ([333, 96, 500], [333, 200, 64], 2, 128, "f16", True, (-1, -1), 0.0),
+    ([70, 3, 130], [70, 40, 130], 2, 48, "f32", True, (20, -1), 0.1),
+]
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("lq,lk,H,d,dtype,causal,window,p", VARLEN)
+def test_varlen(lq, lk, H, d, dtype, causal, window, p, deterministic):
+    import torch
+    print(f"\n[gpu] varlen lq={lq} lk={lk} H={H} d={d} {dtype} causal={causal} window={window} "
+          f"p={p} det={deterministic}", flush=True)
+    spec = _spec(d, causal, window, p)
+    cu_q, cu_k = cumulative(lq), cumulative(lk)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    host = make_tensors((tq, H, d), dtype, 23 + tq + tk,
+                        shapes={"k": (tk, H, d), "v": (tk, H, d)})
+    dev = _upload(host, dtype)
+    cq, ck = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    mq, mk = max(lq), max(lk)
+    o, lse = fa.forward_varlen(dev["q"], dev["k"], dev["v"], cq, ck, mq, mk, **_kw(spec))
+    dq, dk, dv, delta = fa.backward_varlen(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, cq, ck,
+                                           mq, mk, deterministic=deterministic, **_kw(spec))
+    torch.cuda.synchronize()
+    ref = oracle.varlen_backward(host["q"], host["k"], host["v"], host["do"], cu_q, cu_k, spec)
+    mags = {n: float(np.abs(host[n]).max()) for n in ("q", "k", "v", "do")}
+    for name, got in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(name, to_host(got), ref[name], dtype, zero_floor(name, dtype, d, spec.sm_scale, mags))
+    valid = ~np.isnan(ref["lse"])
+    _check_lse(to_host(lse)[valid], ref["lse"][valid])
+    assert_close("delta", to_host(delta)[valid], ref["delta"][valid], dtype)
+
+
+def test_varlen_equals_separate_calls():
+    """Each packed sequence gives bit-identical results to a call on it alone
+    (deterministic mode, same batch index via a one-sequence varlen call)."""
+    import torch
+    lq, lk, H, d = [200, 515, 64], [300, 515, 1], 2, 128
+    spec = _spec(d, True, (-1, -1), 0.0)
+    cu_q, cu_k = cumulative(lq), cumulative(lk)
+    host = make_tensors((int(cu_q[-1]), H, d), "bf16", 5,
+                        shapes={"k": (int(cu_k[-1]), H, d), "v": (int(cu_k[-1]), H, d)})
+    dev = _upload(host, "bf16")
+    cq, ck = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    o, lse = fa.forward_varlen(dev["q"], dev["k"], dev["v"], cq, ck, max(lq), max(lk), **_kw(spec))
+    dq, dk, dv, _ = fa.backward_varlen(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, cq, ck,
+                                       max(lq), max(lk), deterministic=True, **_kw(spec))
+    for b in range(len(lq)):
+        qs, ks = slice(int(cu_q[b]), int(cu_q[b + 1])), slice(int(cu_k[b]), int(cu_k[b + 1]))
+        one = {n: dev[n][qs if n in ("q", "do") else ks].unsqueeze(0).transpose(1, 2)
+               for n in ("q", "k", "v", "do")}
+        o1, l1 = fa.forward(one["q"], one["k"], one["v"], **_kw(spec))
+        dq1, dk1, dv1, _ = fa.backward(one["q"], one["k"], one["v"], o1, one["do"], l1,
+                                       deterministic=True, **_kw(spec))
+        torch.cuda.synchronize()
+        assert torch.equal(o[qs], o1[0].transpose(0, 1)), b
+        assert torch.equal(dq[qs], dq1[0].transpose(0, 1)), b
+        assert torch.equal(dk[ks], dk1[0].transpose(0, 1)), b
+        assert torch.equal(dv[ks], dv1[0].transpose(0, 1)), b
