@@ -101,9 +101,9 @@ def main():
     ap.add_argument("--workload", default="train_causal_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--side-checks", action="store_true",
-                    help="also time fa_fwd and the non-causal backward at the same shape "
-                         "(kept out of the default run so its kernel averages stay those of the "
-                         "timed backward)")
+                    help="also time fa_fwd, the non-causal backward at the same shape and the "
+                         "same tokens packed as variable-length sequences (kept out of the "
+                         "default run so its kernel averages stay those of the timed backward)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -214,6 +214,45 @@ def main():
                                                deterministic=args.mode == "deterministic", **kw_nc),
                            n_side)
         del o_nc, lse_nc
+    # Varlen: the same B * N tokens per head repacked as sequences of mixed
+    # length (seeded, 256..N each, the last one cut to fit), with the
+    # workload's mask applied per sequence; credited with those sequences'
+    # visible pairs.
+    vl = None
+    if args.side_checks:
+        from flashattention_backward_pass_fa_amd.inputs import cumulative, pack_lengths
+        total = w.B * w.N
+        lens = pack_lengths(total, 256, w.N, w.seed + 100)
+        cu = torch.from_numpy(cumulative(lens)).to(dev)
+        pk = {n: t[n].permute(0, 2, 1, 3).reshape(total, w.H, w.d).contiguous()
+              for n in ("q", "k", "v", "do")}
+        o_v, lse_v = fa.forward_varlen(pk["q"], pk["k"], pk["v"], cu, cu, max(lens), max(lens), **kw)
+        # the same two C calls as the timed step, arguments built once
+        vp = fa.make_params((len(lens), w.H, max(lens), w.d), code,
+                            deterministic=args.mode == "deterministic", seqlen_k=max(lens),
+                            cu_seqlens_q=cu.data_ptr(), cu_seqlens_k=cu.data_ptr(), **kw)
+        v_ws_bytes = fa.fa_bwd_workspace_bytes(vp)
+        v_ws = torch.empty(max(v_ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+        v_ws_ptr = ctypes.c_void_p(v_ws.data_ptr() if v_ws_bytes else 0)
+        v_delta = torch.empty((len(lens), w.H, max(lens)), dtype=torch.float32, device=dev)
+        v_out = [torch.empty_like(pk["q"]) for _ in range(3)]
+        T = fa.tensor_arg
+        v_pre = (vp, T(o_v), T(pk["do"]), ctypes.c_void_p(v_delta.data_ptr()), v_ws_ptr)
+        v_bwd = (vp, T(pk["q"]), T(pk["k"]), T(pk["v"]), T(pk["do"]),
+                 ctypes.c_void_p(lse_v.data_ptr()), ctypes.c_void_p(v_delta.data_ptr()),
+                 *(T(x) for x in v_out), v_ws_ptr)
+        v_st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+        def varlen_step():
+            if fa.fa_bwd_preprocess(*v_pre, v_st) or fa.fa_bwd(*v_bwd, v_st):
+                raise RuntimeError("varlen backward failed")
+
+        vl_ms = time_calls(varlen_step, n_side)
+        vl_flops = sum(credited_flops(1, w.H, n, w.d, w.causal, w.window_left, w.window_right)
+                       for n in lens)
+        vl = {"sequences": len(lens), "length_min_max": [min(lens), max(lens)], "tokens": total,
+              "step_ms": round(vl_ms, 4), "tflops": round(vl_flops / (vl_ms * 1e-3) / 1e12, 2)}
+        del pk, o_v, lse_v, v_ws, v_delta, v_out
     deterministic = main_run["deterministic"]
     ms_per_step = main_run["ms_per_step"]
     pre_ms, bwd_ms, step_ms = main_run["pre_ms"], main_run["bwd_ms"], main_run["step_ms"]
@@ -273,6 +312,9 @@ def main():
         line["causal_skip_check"] = {"noncausal_step_ms": round(nc_ms, 4),
                                      "causal_over_noncausal_time": round(ms_per_step / nc_ms, 3),
                                      "visible_fraction": round(flops / credited_flops(w.B, w.H, w.N, w.d), 4)}
+    if vl is not None:
+        vl["tflops_over_fixed"] = round(vl["tflops"] / tflops, 3)
+        line["varlen_check"] = vl
     # A plain copy of known size (outside the timed region): profiling runs
     # use its FETCH_SIZE / WRITE_SIZE to calibrate the HBM byte counters.
     src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)

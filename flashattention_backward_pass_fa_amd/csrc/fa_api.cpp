@@ -34,9 +34,10 @@ fa_status check_params(const fa_params* p) {
     return FA_ERR_INVALID_VALUE;
   if ((int64_t)p->batch * p->heads > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
   if (p->seqlen > kMaxSeq || p->seqlen_k > kMaxSeq) return FA_ERR_NOT_SUPPORTED;
-  // the kernels number their workgroups (one per head and 64 rows) in an int
+  // the kernels number their workgroups (one per head and 64 rows, plus up
+  // to 3 blocks of padding per head) in an int
   const int64_t longest = p->seqlen > p->seqlen_k ? p->seqlen : p->seqlen_k;
-  if ((int64_t)p->batch * p->heads * ((longest + 63) / 64) > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
+  if ((int64_t)p->batch * p->heads * ((longest + 63) / 64 + 3) > INT32_MAX) return FA_ERR_NOT_SUPPORTED;
   // varlen: both offset arrays or neither
   if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_k == nullptr)) return FA_ERR_INVALID_VALUE;
   if (p->cu_seqlens_q && (!aligned(p->cu_seqlens_q, 4) || !aligned(p->cu_seqlens_k, 4)))

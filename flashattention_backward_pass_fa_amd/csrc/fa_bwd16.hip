@@ -240,7 +240,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x, blk = blockIdx.y;
+  int bh, blk;
+  wg_coords(a.m.cu_q != nullptr, bh, blk);
   const int b = bh / a.H, h = bh - b * a.H;
   bwd_localize(a, b);
   const int NQ = a.m.nq, NK = a.m.nk;
@@ -472,7 +473,8 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int grp = w & 3, qh = w >> 2;
-  const int bh = blockIdx.x, blk = blockIdx.y;
+  int bh, blk;
+  wg_coords(a.m.cu_q != nullptr, bh, blk);
   const int b = bh / a.H, h = bh - b * a.H;
   bwd_localize(a, b);
   const int NQ = a.m.nq, NK = a.m.nk;
@@ -674,14 +676,16 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x, blk = blockIdx.y;
+  int bh, blk;
+  wg_coords(a.m.cu_q != nullptr, bh, blk);
   const int b = bh / a.H, h = bh - b * a.H;
   bwd_localize(a, b);
   const int NQ = a.m.nq, NK = a.m.nk;
   // Longest first: with a causal mask the last query blocks see the most keys.
-  const int qblk = a.m.causal ? gridDim.y - 1 - blk : blk;
+  const int nblk = (NQ + C::BQ - 1) / C::BQ;
+  if (blk >= nblk) return;  // past this sequence's queries
+  const int qblk = a.m.causal ? nblk - 1 - blk : blk;
   const int q0 = qblk * C::BQ;
-  if (q0 >= NQ) return;  // past this sequence's queries
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
   const int64_t row_base = (int64_t)bh * a.ln;
@@ -771,11 +775,14 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   }
   __syncthreads();
 
-  // Key blocks [jtA, jtB) are seen by all 128 queries of the block with no
-  // mask edge and no dropout.
+  // Key blocks [jtA, jtB) are seen by all of the block's queries with no
+  // mask edge.  Query rows past the sequence end need no mask: their Q and
+  // dO are zero, so they only add dS = 0 to their own (unstored) dQ rows;
+  // the last real row bounds the left window.
   int jtA = jt1, jtB = jt1;
-  if (q0 + C::BQ <= NQ) {
-    const int lo = max(0, q0 + C::BQ - 1 - a.m.lo_off);
+  {
+    const int qlast = min(q0 + C::BQ, NQ) - 1;
+    const int lo = max(0, qlast - a.m.lo_off);
     const int hi = min(NK - C::BK, q0 + a.m.hi_off - C::BK + 1);
     if (lo <= hi) {
       jtA = min(max(jt0, (lo + C::BK - 1) / C::BK), jt1);
@@ -876,13 +883,14 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
   const int bh = a.B * a.H;
-  const dim3 grid_kv(bh, (a.m.nk + KvCfg<D>::BC - 1) / KvCfg<D>::BC);
+  const bool varlen = a.m.cu_q != nullptr;
+  const dim3 grid_kv(bh, grid_blocks(bh, a.m.nk, KvCfg<D>::BC, varlen));
   if (deterministic) {
     hipLaunchKernelGGL(a.m.dropout ? (dkdv_q2_kernel<D, true>) : (dkdv_q2_kernel<D, false>), grid_kv,
                        dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid_q(bh, (a.m.nq + QCfg<D>::BQ - 1) / QCfg<D>::BQ);
+    const dim3 grid_q(bh, grid_blocks(bh, a.m.nq, QCfg<D>::BQ, varlen));
     hipLaunchKernelGGL(a.m.dropout ? (dq_kernel<D, true>) : (dq_kernel<D, false>), grid_q, dim3(QCfg<D>::NT),
                        0, s, a);
   } else {

@@ -212,6 +212,41 @@ __device__ __forceinline__ const char* row_addr(const char* head, uint32_t rs, i
   return head + (uint64_t)(uint32_t)row * rs;
 }
 
+// Head (bh) and block (blk) of this workgroup, for a grid of (heads,
+// blocks).  The hardware deals workgroup L (linear launch index) to XCD
+// L % 8 and, inside an XCD, hands consecutive workgroups to its shader
+// arrays in turn (measured: with a grid x extent that is a multiple of 32,
+// every workgroup of a head lands on one array).  The plain mapping (x =
+// head, y = block) keeps a head on one XCD (its K, V, Q, dO share that
+// XCD's L2) and gives each array whole heads: right when all heads carry the
+// same work.  Packed variable-length batches (varlen) do not: a long
+// sequence's heads would sit on one array while the others idle on short
+// ones.  There, with the head count a multiple of 8 and the block count of 4
+// (the launchers pad it), L is re-read so that a head still stays on one
+// XCD but each run of four consecutive workgroups of an XCD is four
+// consecutive blocks of one head, one per array, snaking (every other run
+// backwards, which evens out work that falls linearly with the block), and
+// block-major across heads so the longest blocks still start first.
+__device__ __forceinline__ void wg_coords(bool varlen, int& bh, int& blk) {
+  const int nh = gridDim.x, nb = gridDim.y;
+  if (varlen && (nh & 7) == 0 && (nb & 3) == 0) {
+    const int L = blockIdx.y * nh + blockIdx.x;
+    const int k = L >> 3, run = k >> 2, per_xcd = nh >> 3;
+    const int blk4 = run / per_xcd, t = k & 3;
+    bh = (L & 7) + 8 * (run % per_xcd);
+    blk = 4 * blk4 + ((blk4 & 1) ? 3 - t : t);
+  } else {
+    bh = blockIdx.x;
+    blk = blockIdx.y;
+  }
+}
+
+// Block count of a grid over n rows in tiles of `tile` (padded to a multiple
+// of 4 for wg_coords' varlen mapping).
+__host__ __device__ constexpr int grid_blocks(int heads, int n, int tile, bool varlen) {
+  return varlen && heads % 8 == 0 ? ((n + tile - 1) / tile + 3) / 4 * 4 : (n + tile - 1) / tile;
+}
+
 template <typename T>
 __device__ __forceinline__ T* at(const TensorView& t, int b, int h, int n) {
   return (T*)t.ptr + (int64_t)b * t.sb + (int64_t)h * t.sh + (int64_t)n * t.sn;

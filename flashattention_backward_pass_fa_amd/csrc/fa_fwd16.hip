@@ -51,7 +51,8 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   // the wave index is uniform across the wave: keep it (and all derived from it) scalar
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), c = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x, blk = blockIdx.y;
+  int bh, blk;
+  wg_coords(a.m.cu_q != nullptr, bh, blk);
   const int b = bh / a.H, h = bh - b * a.H;
   {
     const SeqRows r = seq_localize(a.m, b);
@@ -64,8 +65,9 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   }
   const int NQ = a.m.nq, NK = a.m.nk;
   // Longest first: with a causal mask the last query blocks see the most keys.
-  const int q0 = (a.m.causal ? gridDim.y - 1 - blk : blk) * C::BQ;
-  if (q0 >= NQ) return;  // past this sequence's queries
+  const int nblk = (NQ + C::BQ - 1) / C::BQ;
+  if (blk >= nblk) return;  // past this sequence's queries
+  const int q0 = (a.m.causal ? nblk - 1 - blk : blk) * C::BQ;
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
 
@@ -198,12 +200,14 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
   };
-  // Key blocks [jtA, jtB) are seen by all 128 queries of the block with no
+  // Key blocks [jtA, jtB) are seen by all of the block's queries with no
   // mask edge: the first query bounds k0 from above (causality, right
-  // window), the last query from below (left window).
+  // window), the last real query from below (left window).  Rows past the
+  // sequence end need no mask: their Q is zero and their O is not stored.
   int jtA = jt1, jtB = jt1;
-  if (q0 + C::BQ <= NQ) {
-    const int lo = max(0, q0 + C::BQ - 1 - a.m.lo_off);
+  {
+    const int qlast = min(q0 + C::BQ, NQ) - 1;
+    const int lo = max(0, qlast - a.m.lo_off);
     const int hi = min(NK - C::BK, q0 + a.m.hi_off - C::BK + 1);
     if (lo <= hi) {
       jtA = min(max(jt0, (lo + C::BK - 1) / C::BK), jt1);
@@ -239,7 +243,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
 }  // namespace
 
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.H, (a.m.nq + 127) / 128);
+  const dim3 grid(a.B * a.H, grid_blocks(a.B * a.H, a.m.nq, 128, a.m.cu_q != nullptr));
   if (a.d == 128)
     hipLaunchKernelGGL(a.m.dropout ? (fwd_kernel<128, true>) : (fwd_kernel<128, false>), grid, dim3(256), 0, s, a);
   else

@@ -11,11 +11,16 @@ V, dO, O (the last for D), L and D, write D, dQ, dK, dV.
 import numpy as np
 
 
-def visible_pairs(n, causal=False, window_left=-1, window_right=-1):
-    """Number of (i, j) with key j visible to query i, in closed form per row."""
-    i = np.arange(n, dtype=np.int64)
+def visible_pairs(n, causal=False, window_left=-1, window_right=-1, n_k=None):
+    """Number of (i, j) with key j visible to query i, in closed form per row.
+
+    n queries over n_k keys (default n); query i stands at key position
+    i + n_k - n (the last query aligned with the last key).
+    """
+    n_k = n if n_k is None else n_k
+    i = np.arange(n, dtype=np.int64) + (n_k - n)
     lo = np.zeros(n, dtype=np.int64)
-    hi = np.full(n, n, dtype=np.int64)
+    hi = np.full(n, n_k, dtype=np.int64)
     if causal:
         hi = np.minimum(hi, i + 1)
     if window_left >= 0:
@@ -25,8 +30,8 @@ def visible_pairs(n, causal=False, window_left=-1, window_right=-1):
     return int(np.maximum(hi - lo, 0).sum())
 
 
-def credited_flops(B, H, n, d, causal=False, window_left=-1, window_right=-1):
-    return 10.0 * d * B * H * visible_pairs(n, causal, window_left, window_right)
+def credited_flops(B, H, n, d, causal=False, window_left=-1, window_right=-1, n_k=None):
+    return 10.0 * d * B * H * visible_pairs(n, causal, window_left, window_right, n_k)
 
 
 def algorithmic_bytes(B, H, n, d, elem_bytes=2):

@@ -87,7 +87,7 @@ typedef struct fa_tensor {
  *   batch, heads  B, H >= 1
  *   seqlen        Nq, queries per sequence, 1 <= Nq <= 2^21
  *   seqlen_k      Nk, keys per sequence, 1 <= Nk <= 2^21;
- *                 B * H * ceil(max(Nq, Nk) / 64) must stay below 2^31
+ *                 B * H * (ceil(max(Nq, Nk) / 64) + 3) must stay below 2^31
  *   head_dim      d: bf16 and fp16 support 64 and 128; fp32 supports 1..128
  *   sm_scale      S = sm_scale * Q K^T (the pages use 1/sqrt(d)); any finite
  *                 value, 0 included

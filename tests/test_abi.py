@@ -97,6 +97,7 @@ VOID = ctypes.c_void_p
     (dict(shape=(1, 1, 70000, 64), dropout_p=0.1), 2),   # dropout counter holds 16-bit indices
     (dict(shape=(1, 1, (1 << 21) + 1, 64)), 2),           # longest sequence is 2^21
     (dict(shape=(1 << 16, 1 << 12, 1 << 10, 64)), 2),     # workgroup count past 2^31
+    (dict(shape=(1 << 15, 1 << 14, 1, 64)), 2),           # 2^29 heads x (1 + 3 padding) blocks
     (dict(seqlen_k=0), 1),
     (dict(seqlen_k=(1 << 21) + 1), 2),                      # keys too
     (dict(shape=(1 << 16, 1 << 12, 64, 64), seqlen_k=1 << 10), 2),  # the longer length counts

@@ -63,6 +63,10 @@ RAGGED = [
     (1, 2, 333, 64, False, (-1, -1), 0.25),
     (1, 2, 600, 128, True, (-1, -1), 0.1),
     (1, 1, 900, 64, False, (64, 64), 0.3),
+    # head counts that are multiples of 8 with block counts padded to 4
+    # (the launch-index remap): 6 -> 8 and 3 -> 4 blocks
+    (2, 4, 700, 64, True, (-1, -1), 0.0),
+    (1, 16, 300, 128, False, (40, 9), 0.1),
 ]
 
 

@@ -86,6 +86,8 @@ VARLEN = [
     ([400, 129, 7], [400, 129, 7], 2, 64, "bf16", True, (-1, -1), 0.2),
     ([333, 96, 500], [333, 200, 64], 2, 128, "f16", True, (-1, -1), 0.0),
     ([70, 3, 130], [70, 40, 130], 2, 48, "f32", True, (20, -1), 0.1),
+    # 6 sequences x 4 heads: the launch-index remap with padded block counts
+    ([900, 5, 300, 1, 640, 77], [900, 5, 300, 1, 640, 77], 4, 128, "bf16", True, (-1, -1), 0.0),
 ]
 
 
