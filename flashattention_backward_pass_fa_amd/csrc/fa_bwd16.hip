@@ -65,6 +65,13 @@ __device__ __forceinline__ e16x8 zero8() {
   return z;
 }
 
+// The KV-outer kernels read rows past a sequence's end as copies of its
+// last row (a clamped index) rather than under a condition: a load under a
+// condition compiles to a branch that waits for it, which turned their
+// prologues into one memory round trip per load.  The copies are finite and
+// every use of them is masked or lands in rows that are never stored.  (The
+// Q-outer kernel keeps zero rows: its clamped form measured slower.)
+
 // Is every (query, key) of rows [q0, q0+rows) x keys [k0, k0+cols) visible?
 __device__ __forceinline__ bool block_full(const MaskArgs& m, int q0, int rows, int k0, int cols) {
   return (q0 + rows <= m.nq) & (k0 + cols <= m.nk) & (k0 >= q0 + rows - 1 - m.lo_off) &
@@ -255,27 +262,6 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
   const int it0 = q_lo / C::BR;
   const int it1 = q_lo < q_hi ? (q_hi + C::BR - 1) / C::BR : it0;
 
-  // This wave's 32 keys: B operands of S = Q K^T and dP = dO V^T.
-  e16x8 kreg[C::KT], vreg[C::KT];
-  {
-    const bool ok = key < NK;
-    const e16* kp = at<e16>(a.k, b, h, ok ? key : 0);
-    const e16* vp = at<e16>(a.v, b, h, ok ? key : 0);
-#pragma unroll
-    for (int t = 0; t < C::KT; ++t) {
-      kreg[t] = ok ? load8(kp + 16 * t + 8 * g) : zero8();
-      vreg[t] = ok ? load8(vp + 16 * t + 8 * g) : zero8();
-    }
-  }
-  // the block's K rows, row-major in LDS: B operand of dQ = dS K
-#pragma unroll
-  for (int x = 0; x < C::BC * C::CH / C::NT; ++x) {
-    const int chunk = tid + x * C::NT;
-    const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-    const int kr = kv0 + row;
-    store8(sK + row * C::LD + col, kr < NK ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
-  }
-
   const int64_t row_base = (int64_t)bh * a.ln;
   e16x8 pq[C::LOADS], po[C::LOADS];
   float pl = 0.f, pd = 0.f;
@@ -286,21 +272,44 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int qr = q0 + row;
-      if (qr < NQ) {
-        pq[x] = load8(at<e16>(a.q, b, h, qr) + col);
-        po[x] = load8(at<e16>(a.dout, b, h, qr) + col);
-      } else {
-        pq[x] = zero8();
-        po[x] = zero8();
-      }
+      const int qc = min(q0 + row, NQ - 1);
+      pq[x] = load8(at<e16>(a.q, b, h, qc) + col);
+      po[x] = load8(at<e16>(a.dout, b, h, qc) + col);
     }
-    if (tid < C::BR) {
-      const int qr = q0 + tid;
-      pl = qr < NQ ? a.lse[row_base + qr] * kLog2e : 0.f;
-      pd = qr < NQ ? a.delta[row_base + qr] : 0.f;
-    }
+    const int qc = min(q0 + (tid & (C::BR - 1)), NQ - 1);  // every thread loads; tid < BR stores
+    pl = a.lse[row_base + qc];  // scaled at the store: arithmetic here would wait for the load
+    pd = a.delta[row_base + qc];
   };
+  if (it0 < it1) load_tile(it0);  // in flight with the K, V loads below
+
+  // This wave's 32 keys: B operands of S = Q K^T and dP = dO V^T.
+  e16x8 kreg[C::KT], vreg[C::KT];
+  {
+    const e16* kp = at<e16>(a.k, b, h, min(key, NK - 1));
+    const e16* vp = at<e16>(a.v, b, h, min(key, NK - 1));
+#pragma unroll
+    for (int t = 0; t < C::KT; ++t) {
+      kreg[t] = load8(kp + 16 * t + 8 * g);
+      vreg[t] = load8(vp + 16 * t + 8 * g);
+    }
+  }
+  // the block's K rows, row-major in LDS: B operand of dQ = dS K
+  {
+    constexpr int KL = C::BC * C::CH / C::NT;
+    e16x8 kx[KL];
+#pragma unroll
+    for (int x = 0; x < KL; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      kx[x] = load8(at<e16>(a.k, b, h, min(kv0 + row, NK - 1)) + col);
+    }
+#pragma unroll
+    for (int x = 0; x < KL; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      store8(sK + row * C::LD + col, kx[x]);
+    }
+  }
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int x = 0; x < C::LOADS; ++x) {
@@ -310,7 +319,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
       store8(&sO[buf][row * C::LD + col], po[x]);
     }
     if (tid < C::BR) {
-      sL[buf][tid] = pl;
+      sL[buf][tid] = pl * kLog2e;
       sD[buf][tid] = pd;
     }
   };
@@ -322,10 +331,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
     dv_acc[n] = f32x16{};
   }
 
-  if (it0 < it1) {
-    load_tile(it0);
-    store_tile(0);
-  }
+  if (it0 < it1) store_tile(0);
   __syncthreads();
 
   for (int it = it0; it < it1; ++it) {
@@ -488,16 +494,6 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   const int it0 = q_lo / C::BR;
   const int it1 = q_lo < q_hi ? (q_hi + C::BR - 1) / C::BR : it0;
 
-  // K and V rows of the block into LDS (zeros past the sequence end)
-#pragma unroll
-  for (int x = 0; x < C::KV_LOADS; ++x) {
-    const int chunk = tid + x * C::NT;
-    const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-    const int kr = kv0 + row;
-    store8(sK + row * C::LD + col, kr < NK ? load8(at<e16>(a.k, b, h, kr) + col) : zero8());
-    store8(sV + row * C::LD + col, kr < NK ? load8(at<e16>(a.v, b, h, kr) + col) : zero8());
-  }
-
   const int64_t row_base = (int64_t)bh * a.ln;
   const char* q_head = (const char*)at<e16>(a.q, b, h, 0);
   const char* o_head = (const char*)at<e16>(a.dout, b, h, 0);
@@ -514,10 +510,8 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
       pq[x] = load8((const e16*)row_addr(q_head, q_rs, qr) + col);
       po[x] = load8((const e16*)row_addr(o_head, o_rs, qr) + col);
     }
-    if (tid < 2 * C::BR) {
-      const int qr = q0 + (tid & (C::BR - 1));
-      pld = qr < NQ ? (tid < C::BR ? a.lse[row_base + qr] * kLog2e : a.delta[row_base + qr]) : 0.f;
-    }
+    if (tid < 2 * C::BR)
+      pld = (tid < C::BR ? a.lse : a.delta)[row_base + min(q0 + (tid & (C::BR - 1)), NQ - 1)];
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -527,7 +521,7 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
       store8(smem + buf * TILE + row * C::LD + col, pq[x]);
       store8(smem + (2 + buf) * TILE + row * C::LD + col, po[x]);
     }
-    if (tid < C::BR) sL[buf][tid] = pld;
+    if (tid < C::BR) sL[buf][tid] = pld * kLog2e;
     else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = pld;
   };
 
@@ -538,10 +532,28 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
     dv_acc[n] = f32x16{};
   }
 
-  if (it0 < it1) {
-    load_tile(it0);
-    store_tile(0);
+  // The first Q/dO block and the block's K and V rows are all loaded before
+  // anything is stored, so the prologue waits for memory once.
+  if (it0 < it1) load_tile(it0);
+  {
+    e16x8 kx[C::KV_LOADS], vx[C::KV_LOADS];
+#pragma unroll
+    for (int x = 0; x < C::KV_LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      const int kc = min(kv0 + row, NK - 1);
+      kx[x] = load8(at<e16>(a.k, b, h, kc) + col);
+      vx[x] = load8(at<e16>(a.v, b, h, kc) + col);
+    }
+#pragma unroll
+    for (int x = 0; x < C::KV_LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      store8(sK + row * C::LD + col, kx[x]);
+      store8(sV + row * C::LD + col, vx[x]);
+    }
   }
+  if (it0 < it1) store_tile(0);
   __syncthreads();
 
   const e16* Kr = sK + (32 * grp + c) * C::LD + 8 * g;  // this lane's key row (B operands)
@@ -714,26 +726,28 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   const char* v_head = (const char*)at<e16>(a.v, b, h, 0);
   const uint32_t k_rs = (uint32_t)a.k.sn * 2, v_rs = (uint32_t)a.v.sn * 2;
   e16x8 pk[C::LOADS], pv[C::LOADS];
-  auto load_tile = [&](int jt) {
+  auto load_into = [&](int jt, e16x8* kd, e16x8* vd) {
     const int k0 = jt * C::BK;
 #pragma unroll
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int kr = min(k0 + row, NK - 1);  // rows past the end are masked: read a valid one
-      pk[x] = load8((const e16*)row_addr(k_head, k_rs, kr) + col);
-      pv[x] = load8((const e16*)row_addr(v_head, v_rs, kr) + col);
+      const int kr = min(k0 + row, NK - 1);
+      kd[x] = load8((const e16*)row_addr(k_head, k_rs, kr) + col);
+      vd[x] = load8((const e16*)row_addr(v_head, v_rs, kr) + col);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_from = [&](int buf, const e16x8* ks, const e16x8* vs) {
 #pragma unroll
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      store8(&sK[buf][row * C::LD + col], pk[x]);
-      store8(&sV[buf][row * C::LD + col], pv[x]);
+      store8(&sK[buf][row * C::LD + col], ks[x]);
+      store8(&sV[buf][row * C::LD + col], vs[x]);
     }
   };
+  auto load_tile = [&](int jt) { load_into(jt, pk, pv); };
+  auto store_tile = [&](int buf) { store_from(buf, pk, pv); };
   auto ring = [&](int jt) { return (jt - jt0) % 3; };
 
   f32x16 dq_acc[C::DT];
@@ -766,12 +780,11 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   };
 
   if (jt0 < jt1) {
+    e16x8 k1[C::LOADS], v1[C::LOADS];
     load_tile(jt0);
+    if (jt0 + 1 < jt1) load_into(jt0 + 1, k1, v1);
     store_tile(0);
-    if (jt0 + 1 < jt1) {
-      load_tile(jt0 + 1);
-      store_tile(1);
-    }
+    if (jt0 + 1 < jt1) store_from(1, k1, v1);
   }
   __syncthreads();
 

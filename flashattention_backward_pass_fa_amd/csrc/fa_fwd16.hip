@@ -71,12 +71,15 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const int qw = q0 + 32 * w;
   const int myq = qw + c;
 
+  // Rows past the end are read as copies of the last row (a clamped index):
+  // a load under a condition compiles to a branch that waits for it.  The
+  // copies are finite; query copies only feed O rows that are never stored,
+  // key copies are masked.
   e16x8 qreg[C::KT];
   {
-    const bool ok = myq < NQ;
-    const e16* qp = at<e16>(a.q, b, h, ok ? myq : 0);
+    const e16* qp = at<e16>(a.q, b, h, min(myq, NQ - 1));
 #pragma unroll
-    for (int t = 0; t < C::KT; ++t) qreg[t] = ok ? load8(qp + 16 * t + 8 * g) : zero8();
+    for (int t = 0; t < C::KT; ++t) qreg[t] = load8(qp + 16 * t + 8 * g);
   }
 
   // Keys that at least one of the block's queries can see (workgroup-uniform;
@@ -93,14 +96,9 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int kr = k0 + row;
-      if (kr < NK) {
-        pk[x] = load8(at<e16>(a.k, b, h, kr) + col);
-        pv[x] = load8(at<e16>(a.v, b, h, kr) + col);
-      } else {
-        pk[x] = zero8();
-        pv[x] = zero8();
-      }
+      const int kc = min(k0 + row, NK - 1);
+      pk[x] = load8(at<e16>(a.k, b, h, kc) + col);
+      pv[x] = load8(at<e16>(a.v, b, h, kc) + col);
     }
   };
   auto store_tile = [&](int buf) {
@@ -203,7 +201,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   // Key blocks [jtA, jtB) are seen by all of the block's queries with no
   // mask edge: the first query bounds k0 from above (causality, right
   // window), the last real query from below (left window).  Rows past the
-  // sequence end need no mask: their Q is zero and their O is not stored.
+  // sequence end need no mask: their O is never stored.
   int jtA = jt1, jtB = jt1;
   {
     const int qlast = min(q0 + C::BQ, NQ) - 1;
