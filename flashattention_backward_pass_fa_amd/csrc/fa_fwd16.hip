@@ -35,12 +35,6 @@ struct FCfg {
 
 __device__ __forceinline__ e16x8 load8(const e16* p) { return *(const e16x8*)p; }
 __device__ __forceinline__ void store8(e16* p, e16x8 v) { *(e16x8*)p = v; }
-__device__ __forceinline__ e16x8 zero8() {
-  e16x8 z;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (e16)0.0f;
-  return z;
-}
 
 template <int D, bool DROP>
 __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
