@@ -10,6 +10,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "../../include/fa.h"
 #include "fa_kernels.h"
@@ -79,6 +80,22 @@ fa_status check_vec(const float* v, uintptr_t align) {
   if (!v) return FA_ERR_INVALID_VALUE;
   if (!aligned(v, align)) return FA_ERR_MISALIGNED;
   return FA_SUCCESS;
+}
+
+// Detectable aliasing (equal base pointers): an output that is also an
+// input, another output or one of the varlen offset arrays.  Null outputs
+// (optional ones) are skipped.
+bool aliased(const fa_params* p, std::initializer_list<const void*> outs,
+             std::initializer_list<const void*> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    if (!*o) continue;
+    if (*o == p->cu_seqlens_q || *o == p->cu_seqlens_k) return true;
+    for (const void* i : ins)
+      if (*o == i) return true;
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (*o == *o2) return true;
+  }
+  return false;
 }
 
 #define FA_TRY(expr)                      \
@@ -167,7 +184,7 @@ fa_status fa_fwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   FA_TRY(check_tensor(p, v));
   FA_TRY(check_tensor(p, o));
   FA_TRY(check_vec(lse, 4));
-  if (o.ptr == q.ptr || o.ptr == k.ptr || o.ptr == v.ptr || o.ptr == (void*)lse) return FA_ERR_INVALID_VALUE;
+  if (aliased(p, {o.ptr, lse}, {q.ptr, k.ptr, v.ptr})) return FA_ERR_INVALID_VALUE;
   FA_TRY(device_ready());
   fa::FwdArgs a{};
   a.q = view(p, q);
@@ -203,8 +220,7 @@ fa_status fa_bwd_preprocess(const fa_params* p, fa_tensor o, fa_tensor dout, flo
   // the accumulator exists only in atomic mode; any other pointer is ignored
   if (!uses_dq_acc(p)) dq_acc = nullptr;
   if (dq_acc) FA_TRY(check_vec(dq_acc, 16));
-  if ((void*)delta == o.ptr || (void*)delta == dout.ptr || (dq_acc && (void*)dq_acc == (void*)delta))
-    return FA_ERR_INVALID_VALUE;
+  if (aliased(p, {delta, dq_acc}, {o.ptr, dout.ptr})) return FA_ERR_INVALID_VALUE;
   FA_TRY(device_ready());
   fa::PrepArgs a{};
   a.o = view(p, o);
@@ -235,15 +251,8 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   FA_TRY(check_vec(delta, 4));
   const bool atomic = uses_dq_acc(p);
   if (atomic) FA_TRY(check_vec(dq_acc, 16));
-  const void* ins[] = {q.ptr, k.ptr, v.ptr, dout.ptr, lse, delta};
-  void* outs[] = {dq.ptr, dk.ptr, dv.ptr, atomic ? (void*)dq_acc : nullptr};
-  for (void* o : outs) {
-    if (!o) continue;
-    for (const void* i : ins)
-      if (o == i) return FA_ERR_INVALID_VALUE;
-  }
-  if (dq.ptr == dk.ptr || dq.ptr == dv.ptr || dk.ptr == dv.ptr) return FA_ERR_INVALID_VALUE;
-  if (atomic && ((void*)dq_acc == dq.ptr || (void*)dq_acc == dk.ptr || (void*)dq_acc == dv.ptr))
+  if (aliased(p, {dq.ptr, dk.ptr, dv.ptr, atomic ? dq_acc : nullptr},
+              {q.ptr, k.ptr, v.ptr, dout.ptr, lse, delta}))
     return FA_ERR_INVALID_VALUE;
   FA_TRY(device_ready());
   fa::BwdArgs a{};

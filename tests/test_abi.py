@@ -139,6 +139,15 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert fa.fa_bwd(p, *args[:4], lse, delta, *args[4:], ws, VOID(0)) == 1
     # debug mask: bad head index
     assert fa.fa_debug_dropout_mask(p, 0, 4, VOID(0x100000), VOID(0)) == 1
+    # two outputs on one buffer
+    args = list(good)
+    args[5] = good[4]
+    assert fa.fa_bwd(p, *args[:4], lse, delta, *args[4:], ws, VOID(0)) == 1
+    # forward: L on an input; an output on a varlen offset array
+    assert fa.fa_fwd(p, *good[:3], good[3], VOID(good[0].ptr), VOID(0)) == 1
+    pv = _params(cu_seqlens_q=0x500000, cu_seqlens_k=0x510000)
+    assert fa.fa_fwd(pv, *good[:3], _t(0x500000), VOID(0x900000), VOID(0)) == 1
+    assert fa.fa_bwd_preprocess(pv, good[0], good[1], VOID(0x510000), VOID(0), VOID(0)) == 1
 
 
 def test_workspace_bytes(lib):
@@ -167,7 +176,7 @@ def test_varlen_ignores_the_batch_stride(lib):
     lse, delta = VOID(0x900000), VOID(0xA00000)
     fixed = _params(deterministic=True)
     assert fa.fa_bwd(fixed, odd, *others[:3], lse, delta, *others[3:], VOID(0), VOID(0)) == 3
-    var = _params(deterministic=True, cu_seqlens_q=0x700000, cu_seqlens_k=0x710000)
+    var = _params(deterministic=True, cu_seqlens_q=0x7100000, cu_seqlens_k=0x7200000)
     assert fa.fa_bwd(var, odd, *others[:3], lse, delta, *others[3:], VOID(0), VOID(0)) == 5
 
 
