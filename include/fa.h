@@ -44,7 +44,9 @@
  *     FA_ERR_MISALIGNED without touching the device.  A failed launch
  *     returns FA_ERR_LAUNCH_FAILED, any other HIP error FA_ERR_HIP.  The
  *     library never aborts and never prints.
- *   - Outputs must not alias inputs or each other.
+ *   - Outputs must not alias inputs, each other or the varlen offset arrays;
+ *     aliasing that shows as equal base pointers returns
+ *     FA_ERR_INVALID_VALUE.
  */
 #ifndef FA_H_
 #define FA_H_
