@@ -464,7 +464,7 @@ struct KvQCfg {
 };
 
 template <int D, bool DROP>
-__global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_q2_body(BwdArgs& a, int bh, int blk) {
   using C = KvQCfg<D>;
   // [0, 4*BR*LD): Q, dO double buffers; then K and V; reused for the
   // partial-sum exchange after the loop.
@@ -479,8 +479,6 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int grp = w & 3, qh = w >> 2;
-  int bh, blk;
-  wg_coords(a.m.cu_q != nullptr, bh, blk);
   const int b = bh / a.H, h = bh - b * a.H;
   bwd_localize(a, b);
   const int NQ = a.m.nq, NK = a.m.nk;
@@ -661,6 +659,13 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
   }
 }
 
+template <int D, bool DROP>
+__global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
+  int bh, blk;
+  wg_coords(a.m.cu_q != nullptr, bh, blk);
+  dkdv_q2_body<D, DROP>(a, bh, blk);
+}
+
 // ---------------------------------------------------------------- Q-outer
 
 // Q-outer dQ kernel with 32-key blocks streamed through a ring of three LDS
@@ -671,25 +676,26 @@ __global__ void __launch_bounds__(512) dkdv_q2_kernel(BwdArgs a) {
 // each iteration issues S^T, dP^T of block j + 1 beside the exponentials and
 // dS of block j, then dQ += dS K of block j; other blocks run the plain
 // per-block sequence with the mask.
-template <int D>
+template <int D, int NT_ = (D == 128 ? 512 : 256)>
 struct QCfg {
-  static constexpr int NT = D == 128 ? 512 : 256, BQ = NT / 2, BK = 32;
+  static constexpr int NT = NT_, BQ = NT / 2, BK = 32;
   static constexpr int MINB = 512 / NT;
   static constexpr int LD = lds_stride(D);
   static constexpr int KT = D / 16, DT = D / 32, CH = D / 8;
-  static constexpr int LOADS = BK * CH / NT;
+  // 16-byte chunks of one 32-key tile; with more threads than chunks the
+  // threads past them move nothing
+  static constexpr int TILE_CHUNKS = BK * CH;
+  static constexpr int LOADS = (TILE_CHUNKS + NT - 1) / NT;
 };
 
-template <int D, bool DROP>
-__global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs a) {
-  using C = QCfg<D>;
+template <int D, bool DROP, int NT>
+__device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
+  using C = QCfg<D, NT>;
   __shared__ __attribute__((aligned(16))) e16 sK[3][C::BK * C::LD];
   __shared__ __attribute__((aligned(16))) e16 sV[3][C::BK * C::LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  int bh, blk;
-  wg_coords(a.m.cu_q != nullptr, bh, blk);
   const int b = bh / a.H, h = bh - b * a.H;
   bwd_localize(a, b);
   const int NQ = a.m.nq, NK = a.m.nk;
@@ -731,6 +737,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 #pragma unroll
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
+      if (C::TILE_CHUNKS % C::NT != 0 && chunk >= C::TILE_CHUNKS) break;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       const int kr = min(k0 + row, NK - 1);
       kd[x] = load8((const e16*)row_addr(k_head, k_rs, kr) + col);
@@ -741,6 +748,7 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
 #pragma unroll
     for (int x = 0; x < C::LOADS; ++x) {
       const int chunk = tid + x * C::NT;
+      if (C::TILE_CHUNKS % C::NT != 0 && chunk >= C::TILE_CHUNKS) break;
       const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
       store8(&sK[buf][row * C::LD + col], ks[x]);
       store8(&sV[buf][row * C::LD + col], vs[x]);
@@ -893,11 +901,44 @@ __global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs 
   }
 }
 
+template <int D, bool DROP>
+__global__ void __launch_bounds__(QCfg<D>::NT, QCfg<D>::MINB) dq_kernel(BwdArgs a) {
+  int bh, blk;
+  wg_coords(a.m.cu_q != nullptr, bh, blk);
+  dq_body<D, DROP, QCfg<D>::NT>(a, bh, blk);
+}
+
+// Small fixed-length problems with d = 64: the KV-outer and the Q-outer
+// workgroups of the deterministic backward in one launch (rows y < nkv are
+// KV blocks, the rest query blocks of 256).  The two parts share only
+// read-only inputs, so when each alone would leave most of the chip idle
+// they run side by side instead of one after the other.  Both parts' LDS
+// fits one workgroup only for d = 64.
+template <int D, bool DROP>
+__global__ void __launch_bounds__(512) bwd_small_kernel(BwdArgs a, int nkv) {
+  static_assert(D == 64, "the two parts' LDS fits one workgroup only for d = 64");
+  if ((int)blockIdx.y < nkv) dkdv_q2_body<D, DROP>(a, blockIdx.x, blockIdx.y);
+  else dq_body<D, DROP, 512>(a, blockIdx.x, blockIdx.y - nkv);
+}
+
+// Workgroups the small-problem launch may have: one per CU of an MI355X, so
+// that all of them are resident at once (one workgroup fits a CU).
+constexpr int kSmallGrid = 256;
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
   const int bh = a.B * a.H;
   const bool varlen = a.m.cu_q != nullptr;
   const dim3 grid_kv(bh, grid_blocks(bh, a.m.nk, KvCfg<D>::BC, varlen));
+  if constexpr (D == 64) {
+    const int nkv = (a.m.nk + KvQCfg<D>::BC - 1) / KvQCfg<D>::BC;
+    const int nq = (a.m.nq + QCfg<D, 512>::BQ - 1) / QCfg<D, 512>::BQ;
+    if (deterministic && !varlen && (int64_t)bh * (nkv + nq) <= kSmallGrid) {
+      hipLaunchKernelGGL(a.m.dropout ? (bwd_small_kernel<D, true>) : (bwd_small_kernel<D, false>),
+                         dim3(bh, nkv + nq), dim3(512), 0, s, a, nkv);
+      return hipGetLastError();
+    }
+  }
   if (deterministic) {
     hipLaunchKernelGGL(a.m.dropout ? (dkdv_q2_kernel<D, true>) : (dkdv_q2_kernel<D, false>), grid_kv,
                        dim3(512), 0, s, a);

@@ -67,6 +67,9 @@ RAGGED = [
     # (the launch-index remap): 6 -> 8 and 3 -> 4 blocks
     (2, 4, 700, 64, True, (-1, -1), 0.0),
     (1, 16, 300, 128, False, (40, 9), 0.1),
+    # d = 64 with too many workgroups for the one-launch small-problem path
+    # (2 * 16 heads x (8 + 4) blocks > 256): the two separate kernels
+    (2, 16, 1000, 64, True, (-1, -1), 0.0),
 ]
 
 
