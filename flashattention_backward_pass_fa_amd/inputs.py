@@ -66,10 +66,14 @@ WORKLOADS = {
 
 
 def round_to_bf16_bits(x):
-    """fp32 values -> bf16 bit patterns (uint16), round to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
-    return (u >> np.uint64(16)).astype(np.uint16)
+    """fp32 values -> bf16 bit patterns (uint16), round to nearest even.
+
+    In 32-bit arithmetic: for every finite or infinite input the bit pattern
+    plus 0x8000 stays below 2**32 (only NaN patterns could wrap).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    u = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (u >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits):

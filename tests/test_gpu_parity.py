@@ -171,3 +171,35 @@ def test_preprocess_writes_workspace_only_in_atomic_mode(dtype, deterministic):
     used = fa.fa_bwd_workspace_bytes(params) > 0
     assert used == (dtype == "bf16" and not deterministic)
     assert torch.all(ws == (0.0 if used else 7.0)).item()
+
+
+def test_longest_sequence_sampled_rows():
+    """N = 2^21, the longest sequence the library takes, with a two-sided
+    window (every row sees at most 251 keys).  Three row ranges [a, b) are
+    checked against the oracle run on the sub-problem of rows and keys
+    [a - wl, b + wr) (the window is translation-invariant, so those rows see
+    the same keys there): O, L, dQ on [a, b), and dK, dV on the keys whose
+    every visible query lies in [a, b), which the sub-problem sums whole."""
+    import numpy as np
+    import oracle
+    from tests.gpu_cases import Case, to_host
+    n, wl, wr = 1 << 21, 200, 50
+    case = Case(1, 1, n, 64, "bf16", window=(wl, wr), seed=21)
+    print(f"\n[gpu] longest {case}", flush=True)
+    host = case.host_inputs()
+    dev = case.device_inputs(host)
+    gpu = case.run_gpu(dev, deterministic=True)
+    got = {name: to_host(gpu[name])[0, 0] for name in ("o", "dq", "dk", "dv")}
+    got_l = to_host(gpu["lse"])[0, 0]
+    spec = case.spec()
+    for a, b in ((0, 4096), (n // 2 - 2048, n // 2 + 2048), (n - 4096, n)):
+        s0, e0 = max(0, a - wl), min(n, b + wr)
+        sub = {name: host[name][0, 0, s0:e0] for name in ("q", "k", "v", "do")}
+        r = oracle.head_backward(sub["q"], sub["k"], sub["v"], sub["do"], spec)
+        for name in ("o", "dq"):
+            assert_close(name, got[name][a:b], r[name][a - s0:b - s0], "bf16")
+        assert float(np.abs(got_l[a:b] - r["lse"][a - s0:b - s0]).max()) <= 1e-3
+        k0 = a + wr if a > 0 else 0
+        k1 = b - wl if b < n else n
+        for name in ("dk", "dv"):
+            assert_close(name, got[name][k0:k1], r[name][k0 - s0:k1 - s0], "bf16")
