@@ -20,6 +20,12 @@
 //                  d = 64) streaming 32-key blocks through a ring of three
 //                  LDS buffers, recomputing S, P, dP, dS to accumulate
 //                  dQ = dS K in registers: the deterministic, atomic-free dQ.
+//  bwd_small_kernel  both deterministic kernels' workgroups in one launch,
+//                  for small fixed-length problems with d = 64 that would
+//                  leave most of the chip idle one kernel at a time.
+//
+// Every kernel first specialises the call to its sequence (lengths, packed
+// rows and the bottom-right alignment folded into the mask offsets).
 //
 // Layout in LDS: Q, dO, K, V tiles are row-major 16-bit with a padded row
 // stride.  The k-inside-lane operands of the dV/dK/dQ products are read
