@@ -203,3 +203,18 @@ def test_longest_sequence_sampled_rows():
         k1 = b - wl if b < n else n
         for name in ("dk", "dv"):
             assert_close(name, got[name][k0:k1], r[name][k0 - s0:k1 - s0], "bf16")
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("dtype,d,causal,window", [
+    ("bf16", 128, True, (-1, -1)),
+    ("bf16", 64, False, (90, 30)),
+    ("f16", 128, True, (-1, -1)),
+    ("f32", 64, True, (-1, -1)),
+])
+def test_sharp_softmax(dtype, d, causal, window, deterministic):
+    """sm_scale = 8/sqrt(d): scores with std ~ 8, nearly one-hot rows, so the
+    exponentials span many orders of magnitude."""
+    import math
+    _run_and_compare(Case(2, 2, 700, d, dtype, causal=causal, window=window, seed=500 + d,
+                          sm_scale=8.0 / math.sqrt(d)), deterministic)
