@@ -634,35 +634,43 @@ __device__ __forceinline__ void dkdv_q2_body(BwdArgs& a, int bh, int blk) {
   }
   for (; it < it1; ++it) step(it, general, no_pre, no_drop);
 
-  // Sum the two query halves of each key group: waves 4..7 hand their
-  // partials to waves 0..3 through LDS (value r of tile n of lane l at
-  // ((grp * 2 DT + n) * 16 + r) * 64 + l, one contiguous KB per register).
-  float* xch = (float*)smem;
-  if (qh == 1) {
+  // dK and dV, one after the other: both query halves write their fp32
+  // partials row-major into LDS (the tiles are free after the loop's last
+  // barrier), then every thread adds the two halves of whole 8-column chunks
+  // and writes them with one 16-byte store (stores of single elements from
+  // the accumulator layout cost most of the kernel's fixed time).  Row
+  // stride XS = D + 8 floats puts the two row groups a wave writes at once
+  // (rows r and r + 4) on opposite halves of the banks.
+  constexpr int XS = D + 8, CPR = D / 8;  // floats per row, 8-column chunks per row
+  static_assert(2 * C::BC * XS * 4 <= (4 * TILE + 2 * KVT) * 2, "partials must fit the tiles' LDS");
+  float* part = (float*)smem;  // [2 halves][BC keys][XS]
+  auto finish = [&](const f32x16* acc, const TensorView& out, float scale) {
 #pragma unroll
     for (int n = 0; n < C::DT; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        xch[((grp * 2 * C::DT + n) * 16 + r) * 64 + lane] = dk_acc[n][r];
-        xch[((grp * 2 * C::DT + C::DT + n) * 16 + r) * 64 + lane] = dv_acc[n][r];
-      }
-  }
-  __syncthreads();
-  if (qh == 0) {
+      for (int r = 0; r < 16; ++r)
+        part[(qh * C::BC + 32 * grp + 8 * (r >> 2) + 4 * g + (r & 3)) * XS + 32 * n + c] = acc[n][r];
+    __syncthreads();
 #pragma unroll
-    for (int n = 0; n < C::DT; ++n) {
+    for (int x = 0; x < C::BC * CPR / C::NT; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / CPR, col = (chunk % CPR) * 8;
+      const float* p0 = part + row * XS + col;
+      const float* p1 = part + (C::BC + row) * XS + col;
+      const f32x4 a0 = *(const f32x4*)p0, a1 = *(const f32x4*)(p0 + 4);
+      const f32x4 b0 = *(const f32x4*)p1, b1 = *(const f32x4*)(p1 + 4);
+      e16x8 v;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float dkv = dk_acc[n][r] + xch[((grp * 2 * C::DT + n) * 16 + r) * 64 + lane];
-        const float dvv = dv_acc[n][r] + xch[((grp * 2 * C::DT + C::DT + n) * 16 + r) * 64 + lane];
-        const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (kr < NK) {
-          at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dkv * a.sm_scale);
-          at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dvv);
-        }
+      for (int e = 0; e < 4; ++e) {
+        v[e] = (e16)((a0[e] + b0[e]) * scale);
+        v[4 + e] = (e16)((a1[e] + b1[e]) * scale);
       }
+      if (kv0 + row < NK) store8(at<e16>(out, b, h, kv0 + row) + col, v);
     }
-  }
+    __syncthreads();
+  };
+  finish(dk_acc, a.dk, a.sm_scale);
+  finish(dv_acc, a.dv, 1.0f);
 }
 
 template <int D, bool DROP>
@@ -697,8 +705,11 @@ struct QCfg {
 template <int D, bool DROP, int NT>
 __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
   using C = QCfg<D, NT>;
-  __shared__ __attribute__((aligned(16))) e16 sK[3][C::BK * C::LD];
-  __shared__ __attribute__((aligned(16))) e16 sV[3][C::BK * C::LD];
+  // the K and V rings (three blocks each), one array so that the final dQ
+  // rows can be staged through it
+  __shared__ __attribute__((aligned(16))) e16 kv_ring[6][C::BK * C::LD];
+  e16 (*sK)[C::BK * C::LD] = kv_ring;
+  e16 (*sV)[C::BK * C::LD] = kv_ring + 3;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
@@ -897,13 +908,35 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
   if (jtA < jtB) fast_range(std::integral_constant<bool, DROP>());
   for (; jt < jt1; ++jt) general(jt);
 
+  // dQ = sm_scale dS K: the waves write their rows (rounded) row-major into
+  // the ring, free after the last block's barrier, and every thread then
+  // writes whole 8-column chunks with 16-byte stores (stores of single
+  // elements from the accumulator layout were the kernel's largest fixed
+  // cost).  When all rows do not fit the ring, two rounds of half the waves.
+  constexpr int SR = D + 8, CPR = D / 8, RING = 6 * C::BK * C::LD;
+  constexpr int ROWS = C::BQ * SR <= RING ? C::BQ : C::BQ / 2;
+  static_assert(ROWS * SR <= RING, "dQ staging must fit the ring");
+  e16* stage = &kv_ring[0][0];
 #pragma unroll
-  for (int n = 0; n < C::DT; ++n) {
+  for (int round = 0; round < C::BQ / ROWS; ++round) {
+    if (w / (ROWS / 32) == round) {
+      const int lw = w % (ROWS / 32);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = qw + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (qr < NQ) at<e16>(a.dq, b, h, qr)[32 * n + c] = (e16)(dq_acc[n][r] * a.sm_scale);
+      for (int n = 0; n < C::DT; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          stage[(32 * lw + 8 * (r >> 2) + 4 * g + (r & 3)) * SR + 32 * n + c] =
+              (e16)(dq_acc[n][r] * a.sm_scale);
     }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < ROWS * CPR / C::NT; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / CPR, col = (chunk % CPR) * 8;
+      const int qr = q0 + round * ROWS + row;
+      if (qr < NQ) store8(at<e16>(a.dq, b, h, qr) + col, *(const e16x8*)(stage + row * SR + col));
+    }
+    if (round + 1 < C::BQ / ROWS) __syncthreads();
   }
 }
 
