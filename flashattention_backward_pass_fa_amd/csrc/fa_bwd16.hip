@@ -798,17 +798,21 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
                                  dq_acc[n]);
     }
   };
-  // the end of every iteration: publish block jt + 2, wait for all waves
-  auto advance = [&](int jt) {
+  // The start of every iteration publishes block jt + 2, whose loads were
+  // issued one iteration earlier (its buffer held block jt - 1, free since
+  // the last barrier; it is first read after this iteration's barrier), and
+  // issues block jt + 3's loads.
+  auto prefetch = [&](int jt) {
     if (jt + 2 < jt1) store_tile(ring(jt + 2));
-    lds_barrier();
+    if (jt + 3 < jt1) load_tile(jt + 3);
   };
 
   if (jt0 < jt1) {
-    e16x8 k1[C::LOADS], v1[C::LOADS];
-    load_tile(jt0);
+    e16x8 k0[C::LOADS], v0[C::LOADS], k1[C::LOADS], v1[C::LOADS];
+    load_into(jt0, k0, v0);
     if (jt0 + 1 < jt1) load_into(jt0 + 1, k1, v1);
-    store_tile(0);
+    if (jt0 + 2 < jt1) load_tile(jt0 + 2);
+    store_from(0, k0, v0);
     if (jt0 + 1 < jt1) store_from(1, k1, v1);
   }
   __syncthreads();
@@ -829,7 +833,7 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
   }
 
   auto general = [&](int jt) {
-    if (jt + 2 < jt1) load_tile(jt + 2);
+    prefetch(jt);
     const int buf = ring(jt);
     const int ks = jt * C::BK;
     if (!block_dead(a.m, qw, 32, ks, 32)) {
@@ -854,7 +858,7 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
       }
       dqmm(buf, d0, d1);
     }
-    advance(jt);
+    lds_barrier();
   };
 
   int jt = jt0;
@@ -879,7 +883,7 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
     f32x16 st, dpt;
     sdp(ring(jtA), st, dpt);
     for (; jt + 1 < jtB; ++jt) {
-      if (jt + 2 < jt1) load_tile(jt + 2);
+      prefetch(jt);
       f32x16 st_n, dpt_n;
       sdp(ring(jt + 1), st_n, dpt_n);
       const e16* Kc = sK[ring(jt)];
@@ -894,15 +898,15 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
       for (int n = 0; n < C::DT; ++n) dq_acc[n] = mfma32x32x16(d0, b0[n], dq_acc[n]);
 #pragma unroll
       for (int n = 0; n < C::DT; ++n) dq_acc[n] = mfma32x32x16(d1, b1[n], dq_acc[n]);
-      advance(jt);
+      lds_barrier();
       st = st_n;
       dpt = dpt_n;
     }
-    if (jt + 2 < jt1) load_tile(jt + 2);
+    prefetch(jt);
     e16x8 d0, d1;
     ds_of(jt, st, dpt, d0, d1);
     dqmm(ring(jt), d0, d1);
-    advance(jt);
+    lds_barrier();
     ++jt;
   };
   if (jtA < jtB) fast_range(std::integral_constant<bool, DROP>());
