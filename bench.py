@@ -107,8 +107,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the backward is "
-              "measured on one GPU's share; see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): every (b, h) of "
+              "the backward is independent, so G GPUs would each run these kernels on B*H/G heads; "
+              "what is measured here is one GPU's share", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

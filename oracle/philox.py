@@ -7,8 +7,9 @@ The dropout rule comes from "Lecture 7 - Backward Pass and Validation",
 section "Dropout": the kernel draws a Bernoulli keep mask from a Philox
 generator seeded by (seed, offset), and a checker must draw the same mask.
 The page gives no mapping from (seed, offset, element) to Philox words, so
-this oracle fixes one (the reading recorded in the design doc).  Each Philox
-block serves four consecutive keys of one row:
+this oracle fixes one: the seed is the key, the offset the low counter
+words, the element the high ones.  Each Philox block serves four
+consecutive keys of one row:
 
     key     = (low 32 bits of seed, high 32 bits of seed)
     counter = (low 32 bits of offset, high 32 bits of offset,
