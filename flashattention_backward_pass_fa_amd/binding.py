@@ -181,6 +181,40 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _validate(q, k, v, o=None, dout=None, lse=None, lse_shape=None, varlen=False):
+    """Host-side checks of the helpers' tensors, before anything is launched.
+
+    The C ABI receives raw pointers and cannot see sizes, so a tensor that
+    disagrees with q's shape would be read or written out of bounds there.
+    """
+    want_dim = 3 if varlen else 4
+    if q.dim() != want_dim or k.dim() != want_dim or v.dim() != want_dim:
+        raise ValueError(f"q, k, v must be {want_dim}-D ({'[total, H, d]' if varlen else '[B, H, N, d]'})")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t is None:
+            continue
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must have q's dtype and device")
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must have the same shape")
+    same = (1, 2) if varlen else (0, 1, 3)  # heads and d; batch too when not packed
+    if any(q.shape[i] != k.shape[i] for i in same):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    for name, t in (("o", o), ("dout", dout)):
+        if t is not None and t.shape != q.shape:
+            raise ValueError(f"{name} {tuple(t.shape)} must have q's shape {tuple(q.shape)}")
+    if lse is not None:
+        _check_f32(lse, "lse", lse_shape, q.device)
+    if not q.is_cuda:
+        raise ValueError("the tensors must be on a GPU")
+
+
+def _check_f32(t, name, shape, device):
+    import torch
+    if t.dtype != torch.float32 or t.device != device or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} on {device}")
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -196,6 +230,7 @@ def forward(q, k, v, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0
             offset=0, stream=None):
     """O (dtype of q) and L (fp32 [B, H, N]) of softmax attention on q, k, v."""
     import torch
+    _validate(q, k, v)
     params = make_params(tuple(q.shape), _dtype_code(q), sm_scale, causal, window, dropout_p,
                          seed, offset, seqlen_k=k.shape[2])
     o = torch.empty_like(q)
@@ -213,6 +248,7 @@ def backward(q, k, v, o, dout, lse, sm_scale=None, causal=False, window=(-1, -1)
     (atomic mode); allocated here when None.  delta: optional fp32 [B, H, N]
     output for D.  Returns (dq, dk, dv, delta).
     """
+    _validate(q, k, v, o, dout, lse, tuple(q.shape[:3]))
     params = make_params(tuple(q.shape), _dtype_code(q), sm_scale, causal, window, dropout_p,
                          seed, offset, deterministic, seqlen_k=k.shape[2])
     return _backward(params, q, k, v, o, dout, lse, q.shape[:3], stream, workspace, delta)
@@ -223,9 +259,14 @@ def _backward(params, q, k, v, o, dout, lse, delta_shape, stream, workspace, del
     st = _stream(stream)
     if delta is None:
         delta = torch.empty(delta_shape, dtype=torch.float32, device=q.device)
+    else:
+        _check_f32(delta, "delta", delta_shape, q.device)
     ws_bytes = fa_bwd_workspace_bytes(params)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device)
+    elif ws_bytes and (workspace.dtype != torch.float32 or workspace.device != q.device
+                       or not workspace.is_contiguous() or workspace.numel() * 4 < ws_bytes):
+        raise ValueError(f"workspace must be a contiguous float32 tensor of at least {ws_bytes} bytes on {q.device}")
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else ctypes.c_void_p(0)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     _check(fa_bwd_preprocess(params, tensor_arg(o), tensor_arg(dout),
@@ -261,6 +302,7 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     past a sequence's length are not written).
     """
     import torch
+    _validate(q, k, v, varlen=True)
     params = _varlen_params(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale,
                             causal, window, dropout_p, seed, offset)
     o = torch.empty_like(q)
@@ -276,12 +318,16 @@ def backward_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
                     deterministic=False, stream=None, workspace=None, delta=None):
     """Packed variable-length backward; tensors as in forward_varlen.
 
-    Returns (dq, dk, dv, delta) with delta [B, H, max_seqlen_q].
+    Returns (dq, dk, dv, delta) with delta [B, H, max_seqlen_q].  The offset
+    values themselves stay on the device unread here: the caller guarantees
+    that they rise from 0 to at most the packed row count (the kernels clamp
+    each length to the longest one).
     """
     params = _varlen_params(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale,
                             causal, window, dropout_p, seed, offset, deterministic)
-    return _backward(params, q, k, v, o, dout, lse, (params.batch, q.shape[1], params.seqlen),
-                     stream, workspace, delta)
+    shape_l = (params.batch, q.shape[1], params.seqlen)
+    _validate(q, k, v, o, dout, lse, shape_l, varlen=True)
+    return _backward(params, q, k, v, o, dout, lse, shape_l, stream, workspace, delta)
 
 
 def debug_dropout_mask(shape, b, h, dropout_p, seed, offset=0, device="cuda", stream=None,
