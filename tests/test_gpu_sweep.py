@@ -1,7 +1,8 @@
 """Seeded random sweep of small problems through the C ABI against the fp64
 oracle: every flag combined with every other (dtype, head dim, unequal
-lengths, varlen batches, causal, windows, dropout, sm_scale, dQ mode), so
-that an interaction no hand-picked case covers still meets the bar."""
+lengths, varlen batches, causal, windows, dropout, sm_scale, dQ mode, and
+[B, N, H, d] storage read and written through strides), so that an
+interaction no hand-picked case covers still meets the bar."""
 
 import math
 
@@ -15,7 +16,7 @@ from tests.gpu_cases import assert_close, to_device, to_host, zero_floor
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 80
 
 
 def _draw(i):
@@ -42,7 +43,14 @@ def _draw(i):
         cfg["B"] = int(r.integers(1, 3))
         cfg["Nq"] = int(r.integers(1, 700))
         cfg["Nk"] = cfg["Nq"] if r.random() < 0.5 else int(r.integers(1, 700))
+        # drawn last, so that the cases drawn before this option existed are unchanged
+        cfg["bnhd"] = bool(r.random() < 0.35)
     return cfg
+
+
+def _bnhd(t):
+    """The same [B, H, N, d] values stored as [B, N, H, d]: a strided view."""
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
 
 
 def _kw(spec):
@@ -67,6 +75,8 @@ def test_random_configuration(i):
         shapes = {"k": (c["B"], H, c["Nk"], d), "v": (c["B"], H, c["Nk"], d)}
         host = make_tensors((c["B"], H, c["Nq"], d), dtype, c["seed"], shapes=shapes)
     dev = {n: to_device(host[n], host.get(n + "_bits"), dtype) for n in ("q", "k", "v", "do")}
+    if c.get("bnhd"):
+        dev = {n: _bnhd(t) for n, t in dev.items()}
     if c["varlen"]:
         cq, ck = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
         mq, mk = max(c["lq"]), max(c["lk"])
