@@ -89,3 +89,37 @@ def test_window_support_of_one_row(N, d, i, wl, wr, deterministic):
     others = np.ones(N, dtype=bool)
     others[i] = False
     assert np.all(q_rows[:, :, others] == 0), "dQ non-zero on rows whose dO is zero"
+
+
+_MANY_HEADS = {}
+
+
+def _many_heads_inputs(shape):
+    """Drawn once for both dQ modes (a 70000-head draw takes seconds)."""
+    if shape not in _MANY_HEADS:
+        _MANY_HEADS[shape] = make_tensors(shape, "bf16", 33)
+    return _MANY_HEADS[shape]
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_more_heads_than_a_16_bit_grid_dimension(deterministic):
+    """B * H = 70000 workgroup columns (past 65535): sampled heads on both
+    sides of 2^16 against the oracle."""
+    import math
+    import torch
+    import oracle
+    from tests.gpu_cases import assert_close
+    B, H, N, d = 1, 70000, 8, 64
+    print(f"\n[gpu] {B}x{H}x{N}x{d} bf16 causal det={deterministic}", flush=True)
+    host = _many_heads_inputs((B, H, N, d))
+    dev = {n: to_device(host[n], host.get(n + "_bits"), "bf16") for n in ("q", "k", "v", "do")}
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=True)
+    dq, dk, dv, _ = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True,
+                                deterministic=deterministic)
+    torch.cuda.synchronize()
+    spec = oracle.Spec(sm_scale=1.0 / math.sqrt(d), causal=True)
+    for h in (0, 1, 40000, 65535, 65536, 69999):
+        ref = oracle.head_backward(host["q"][0, h], host["k"][0, h], host["v"][0, h], host["do"][0, h],
+                                   spec, 0, h)
+        for name, got in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+            assert_close(f"{name}[h={h}]", to_host(got[0, h]), ref[name], "bf16")
