@@ -75,3 +75,17 @@ def test_varlen_rejects_mismatched_packing():
         fa._validate(_t(1, 70, H, D), _t(1, 90, H, D), _t(1, 90, H, D), varlen=True)
     with pytest.raises(ValueError, match="disagree"):
         fa._validate(q, _t(90, H, 32), _t(90, H, 32), varlen=True)
+
+
+def test_missing_library_fails_loudly():
+    """No fallback: a process whose library is not built gets an error on
+    first use (run in a fresh interpreter, before anything is loaded)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import flashattention_backward_pass_fa_amd.binding as b\n"
+            "try:\n    b.load_library('/nonexistent/libfa.so')\n"
+            "except RuntimeError as e:\n    print('raised:', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert "raised:" in out.stdout and "not built" in out.stdout, out.stdout + out.stderr
