@@ -60,6 +60,12 @@ def measured_traffic(mode):
     return float(m_bytes.group(1))
 
 
+def device_info(torch, dev):
+    """Name, architecture and CU count as torch reports them."""
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": p.gcnArchName.split(":")[0], "compute_units": p.multi_processor_count}
+
+
 def cpu_baseline(w, host):
     """The fp64 oracle on one head of the workload, on this host's cores."""
     import oracle
@@ -303,7 +309,7 @@ def main():
         "other_mode": {"dq_mode": other_mode,
                        "ms_per_step": round(other_run["ms_per_step"], 4),
                        "value": round(flops / (other_run["ms_per_step"] * 1e-3) / 1e12, 2)},
-        "device": torch.cuda.get_device_name(dev),
+        "device": device_info(torch, dev),
     }
     fwd_flops = flops * 4 / 10  # forward: S and O products, 4 d per visible pair
     if fwd_ms is not None:
