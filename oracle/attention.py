@@ -29,9 +29,10 @@ for that case; this oracle aligns the last query with the last key, so query
 i stands at key position i + Nk - Nq for the causal and window tests.  A row
 that then sees no key has an empty softmax sum: L = log 0 = -inf, P = 0,
 O = 0, and every gradient through it is 0.  Variable-length batches
-(varlen_backward) are each sequence on its own, with its batch index b.  Dropout is differentiated by the
-chain rule through P~ (the pages do not derive it); the same D is correct
-because sum_j P_ij dP_ij = sum_j P~_ij (dO_i . V_j) = dO_i . O_i.
+(varlen_backward) are each sequence on its own, with its batch index b.
+Dropout is differentiated by the chain rule through P~ (the pages do not
+derive it); the same D is correct because
+sum_j P_ij dP_ij = sum_j P~_ij (dO_i . V_j) = dO_i . O_i.
 
 Rows are processed in groups only to bound memory: every row always sees its
 complete key row, and dK/dV are the plain sum of the per-row contributions.
