@@ -144,7 +144,7 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
         pdrop = p;
         if (DROPOK && a.m.dropout) {
           const bool keep = (kq[e] >> (4 * rr + t)) & 1u;
-          pdrop = keep ? p * a.m.keep_scale : 0.f;
+          pdrop = keep ? p : 0.f;  // 1 / (1 - p) is applied to dV at the store
           dpv = keep ? dpv * a.m.keep_scale : 0.f;
         }
       }
@@ -209,7 +209,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
       const int r = 4 * rr + e;
       p[r] = fast_exp2(sacc[r] * a.scale_log2 - l4[e]);
       const bool keep = !DROP || ((kq[e] >> (4 * rr + kt4)) & 1u);
-      pa[r >> 3][r & 7] = (e16)(DROP ? (keep ? p[r] * a.m.keep_scale : 0.f) : p[r]);
+      pa[r >> 3][r & 7] = (e16)(DROP ? (keep ? p[r] : 0.f) : p[r]);  // 1 / (1 - p) at the dV store
     }
   }
 #pragma unroll
@@ -437,7 +437,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
     lds_barrier();
   }
 
-  // dK = sm_scale * dS^T Q, dV = P~^T dO: one rounding to the element type at the store.
+  // dK = sm_scale * dS^T Q, dV = (Z o P)^T dO / (1 - p): one rounding to the element type at the store.
 #pragma unroll
   for (int n = 0; n < C::DT; ++n) {
 #pragma unroll
@@ -445,7 +445,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
       const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (kr < NK) {
         at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dk_acc[n][r] * a.sm_scale);
-        at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dv_acc[n][r]);
+        at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dv_acc[n][r] * a.m.keep_scale);
       }
     }
   }
@@ -670,7 +670,7 @@ __device__ __forceinline__ void dkdv_q2_body(BwdArgs& a, int bh, int blk) {
     __syncthreads();
   };
   finish(dk_acc, a.dk, a.sm_scale);
-  finish(dv_acc, a.dv, 1.0f);
+  finish(dv_acc, a.dv, a.m.keep_scale);  // 1 / (1 - p): exactly 1 without dropout
 }
 
 template <int D, bool DROP>

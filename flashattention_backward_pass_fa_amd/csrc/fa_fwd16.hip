@@ -8,8 +8,10 @@
 // lanes index queries: the running max m and sum l of the online softmax
 // are then per-lane scalars (one exchange with the other lane half per
 // block), and O^T += V^T P~^T keeps the query index across lanes too, so the
-// per-row rescale is a per-lane multiply.  Dropout multiplies the weights
-// that feed O but not the normaliser l.
+// per-row rescale is a per-lane multiply.  Dropout zeroes the dropped
+// weights that feed O (never the normaliser l); the kept ones enter the
+// 16-bit product unscaled and 1 / (1 - p) joins 1 / l at the end, so the
+// weight of a row's largest score (exactly 1) is not rounded.
 
 #include <type_traits>
 
@@ -198,7 +200,7 @@ __global__ void __launch_bounds__(FCfg<D>::NT, FCfg<D>::MINB) fwd_kernel(FwdArgs
           const float p = fast_exp2(st[kt][r] - m_use);
           l_run += p;
           float pd = p;
-          if (DROP) pd = (keep >> e) & 1u ? p * a.m.keep_scale : 0.f;
+          if (DROP) pd = (keep >> e) & 1u ? p : 0.f;  // 1 / (1 - p) joins 1 / l at the end
           pb[2 * kt + (r >> 3)][r & 7] = (e16)pd;
         }
       }
@@ -284,7 +286,7 @@ __global__ void __launch_bounds__(FCfg<D>::NT, FCfg<D>::MINB) fwd_kernel(FwdArgs
   if (myq < NQ) {
     // a row that sees no key (possible when nq > nk, or through a window)
     // has an empty sum: O = 0 and L = log 0 = -inf
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (DROP ? a.m.keep_scale / l_tot : 1.0f / l_tot) : 0.f;
     e16* op = at<e16>(a.o, b, h, myq);
 #pragma unroll
     for (int n = 0; n < C::DT; ++n) {
