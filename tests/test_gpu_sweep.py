@@ -17,6 +17,10 @@ from tests.gpu_cases import assert_close, to_device, to_host, zero_floor
 pytestmark = pytest.mark.gpu
 
 N_CASES = 80
+# configurations from a longer run of the same generator that once failed:
+# 491, a 3-row dropout problem whose single-key row must give dQ = 0 (the
+# kept weight was rounded with its 1 / (1 - p) factor, biasing D)
+REGRESSIONS = [491]
 
 
 def _draw(i):
@@ -59,7 +63,7 @@ def _kw(spec):
                 seed=spec.seed, offset=spec.offset)
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", list(range(N_CASES)) + REGRESSIONS)
 def test_random_configuration(i):
     import torch
     c = _draw(i)
