@@ -215,9 +215,13 @@ def _check_f32(t, name, shape, device):
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} on {device}")
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The caller's stream, else the current stream of the tensors' device
+    (which need not be the current device); it must belong to that device."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if s.device != torch.device(device) and torch.device(device).index is not None:
+        raise ValueError(f"stream is on {s.device}, the tensors on {device}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -235,8 +239,9 @@ def forward(q, k, v, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0
                          seed, offset, seqlen_k=k.shape[2])
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
-                  ctypes.c_void_p(lse.data_ptr()), _stream(stream)), "fa_fwd")
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
+                      ctypes.c_void_p(lse.data_ptr()), _stream(stream, q.device)), "fa_fwd")
     return o, lse
 
 
@@ -256,7 +261,7 @@ def backward(q, k, v, o, dout, lse, sm_scale=None, causal=False, window=(-1, -1)
 
 def _backward(params, q, k, v, o, dout, lse, delta_shape, stream, workspace, delta):
     import torch
-    st = _stream(stream)
+    st = _stream(stream, q.device)
     if delta is None:
         delta = torch.empty(delta_shape, dtype=torch.float32, device=q.device)
     else:
@@ -269,11 +274,12 @@ def _backward(params, q, k, v, o, dout, lse, delta_shape, stream, workspace, del
         raise ValueError(f"workspace must be a contiguous float32 tensor of at least {ws_bytes} bytes on {q.device}")
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else ctypes.c_void_p(0)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    _check(fa_bwd_preprocess(params, tensor_arg(o), tensor_arg(dout),
-                             ctypes.c_void_p(delta.data_ptr()), ws_ptr, st), "fa_bwd_preprocess")
-    _check(fa_bwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(dout),
-                  ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
-                  tensor_arg(dq), tensor_arg(dk), tensor_arg(dv), ws_ptr, st), "fa_bwd")
+    with torch.cuda.device(q.device):
+        _check(fa_bwd_preprocess(params, tensor_arg(o), tensor_arg(dout),
+                                 ctypes.c_void_p(delta.data_ptr()), ws_ptr, st), "fa_bwd_preprocess")
+        _check(fa_bwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(dout),
+                      ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                      tensor_arg(dq), tensor_arg(dk), tensor_arg(dv), ws_ptr, st), "fa_bwd")
     return dq, dk, dv, delta
 
 
@@ -308,8 +314,9 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     o = torch.empty_like(q)
     lse = torch.empty((params.batch, q.shape[1], params.seqlen), dtype=torch.float32,
                       device=q.device)
-    _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
-                  ctypes.c_void_p(lse.data_ptr()), _stream(stream)), "fa_fwd")
+    with torch.cuda.device(q.device):
+        _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
+                      ctypes.c_void_p(lse.data_ptr()), _stream(stream, q.device)), "fa_fwd")
     return o, lse
 
 
@@ -338,6 +345,7 @@ def debug_dropout_mask(shape, b, h, dropout_p, seed, offset=0, device="cuda", st
                          seqlen_k=seqlen_k)
     n = shape[2]
     mask = torch.empty((n, params.seqlen_k), dtype=torch.uint8, device=device)
-    _check(fa_debug_dropout_mask(params, b, h, ctypes.c_void_p(mask.data_ptr()), _stream(stream)),
-           "fa_debug_dropout_mask")
+    with torch.cuda.device(mask.device):
+        _check(fa_debug_dropout_mask(params, b, h, ctypes.c_void_p(mask.data_ptr()),
+                                     _stream(stream, mask.device)), "fa_debug_dropout_mask")
     return mask
