@@ -36,7 +36,9 @@
  *     no device memory, keeps no pointer after a call returns and holds no
  *     mutable global state; calls are re-entrant.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
- *     default stream) and the call returns after launch.  FA_SUCCESS means
+ *     default stream) and the call returns after launch.  Kernels run on the
+ *     calling thread's current HIP device: the buffers and `stream` must
+ *     belong to it.  FA_SUCCESS means
  *     the arguments were valid and every launch was accepted; faults during
  *     execution surface at the caller's next synchronisation.
  *   - Errors: every argument is validated before any HIP call, so a bad
