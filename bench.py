@@ -101,8 +101,8 @@ def cpu_baseline(w, host):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", choices=["atomic", "deterministic"], default="deterministic")
     ap.add_argument("--workload", default="train_causal_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
