@@ -13,11 +13,11 @@ unit roundoff, whatever the kernels do.
 The model below is the oracle with only the method's 16-bit rounding points
 added: the forward's unnormalised weights and its stored O, and dS before
 the dQ and dK products, each rounded to bf16 (round to nearest even); every
-sum stays in fp64.  Three configurations from long runs of the GPU sweep's
-generator miss the bars under this model, with the same figures the GPU
-gave; those configurations are not among the committed GPU cases.  On the
-configurations that the committed sweep does check, the model meets every
-bar, so it is not a loose stand-in."""
+sum stays in fp64.  Eight configurations from long runs of the GPU sweep's
+generator miss the bars under this model, with the figures the GPU gave to
+within a few per cent; they are not among the committed GPU cases.  On the
+bf16 configurations that the committed sweep does check, the model meets
+every bar, so it is not a loose stand-in."""
 
 import numpy as np
 import pytest
@@ -57,14 +57,26 @@ def _model_head(q, k, v, do, spec, b, h):
     return {"dq": spec.sm_scale * (ds @ np.asarray(k, np.float64)[lo:hi]), "dk": dk, "delta": d_row}
 
 
-def _varlen_case(i):
-    """Sweep configuration i (a packed bf16 batch): host inputs, the oracle's
-    result and the model's, in the layouts the GPU sweep compares."""
+def _case(i):
+    """Sweep configuration i (bf16): the oracle's result and the model's, in
+    the layouts the GPU sweep compares, and the inputs' magnitudes."""
     c = _draw(i)
-    assert c["varlen"] and c["dtype"] == "bf16"
+    assert c["dtype"] == "bf16"
     spec = oracle.Spec(sm_scale=c["scale"], causal=c["causal"], window_left=c["window"][0],
                        window_right=c["window"][1], dropout_p=c["p"], seed=77 + i, offset=i)
     H, d = c["H"], c["d"]
+    if not c["varlen"]:
+        kv = (c["B"], H, c["Nk"], d)
+        host = make_tensors((c["B"], H, c["Nq"], d), "bf16", c["seed"], shapes={"k": kv, "v": kv})
+        ref = oracle.backward(host["q"], host["k"], host["v"], host["do"], spec)
+        model = {n: np.zeros(ref[n].shape) for n in ("dq", "dk", "delta")}
+        for b in range(c["B"]):
+            for h in range(H):
+                r = _model_head(host["q"][b, h], host["k"][b, h], host["v"][b, h], host["do"][b, h], spec, b, h)
+                for n in model:
+                    model[n][b, h] = r[n]
+        mags = {n: float(np.abs(host[n]).max()) for n in ("q", "k", "v", "do")}
+        return c, spec, ref, model, mags
     cu_q, cu_k = cumulative(c["lq"]), cumulative(c["lk"])
     kv = (int(cu_k[-1]), H, d)
     host = make_tensors((int(cu_q[-1]), H, d), "bf16", c["seed"], shapes={"k": kv, "v": kv})
@@ -100,18 +112,23 @@ def _check(name, c, spec, ref, model, mags):
     (6936, "delta", "fro"),
     # 212 queries over 2 keys: two live rows per head, one of them single-key
     (19313, "dq", "fro"),
+    (24832, "dq", "fro"),     # 262 queries over 2 keys, the same shape of problem
+    (24551, "delta", "max"),  # one query over 316 keys
+    (24585, "delta", "fro"),  # 2 x 2, causal: the first row sees one key
+    (26382, "dk", "fro"),     # 2 x 2
+    (26888, "dk", "max"),     # a packed sequence of 52 queries over a single key
 ])
 def test_model_misses_the_bar(i, name, reading):
-    c, spec, ref, model, mags = _varlen_case(i)
+    c, spec, ref, model, mags = _case(i)
     with pytest.raises(AssertionError, match="max" if reading == "max" else "Frobenius"):
         _check(name, c, spec, ref, model, mags)
 
 
-_CHECKED = [i for i in range(N_CASES) if _draw(i)["varlen"] and _draw(i)["dtype"] == "bf16"]
+_CHECKED = [i for i in range(N_CASES) if _draw(i)["dtype"] == "bf16"]
 
 
 @pytest.mark.parametrize("i", _CHECKED)
 def test_model_meets_the_bars_on_the_committed_sweep(i):
-    c, spec, ref, model, mags = _varlen_case(i)
+    c, spec, ref, model, mags = _case(i)
     for name in ("dq", "dk", "delta"):
         _check(name, c, spec, ref, model, mags)
