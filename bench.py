@@ -35,6 +35,9 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_bwd16.hip",
                   "flashattention_backward_pass_fa_amd/csrc/fa_device.h"]
 TRAFFIC_FILE = "profiles/fa_bwd_{mode}_train_causal_bf16_traffic.md"
+KERNELS_FILE = "profiles/fa_bwd_train_causal_bf16_kernels.md"
+CLOCK_FILE = "profiles/fa_bwd_train_causal_bf16_clock.md"
+PEAK_CLOCK_MHZ = 2400.0     # the clock PEAK_BF16_TFLOPS is quoted at
 COPY_CALIBRATION_BYTES = 256 << 20   # one plain device copy, for HBM counter calibration
 
 
@@ -58,6 +61,54 @@ def measured_traffic(mode):
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def _profile_text(rel):
+    """A committed profile summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, rel)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    return text if m_hash and m_hash.group(1) == kernel_source_hash() else None
+
+
+def profiled_kernel_ms(mode):
+    """Average duration (ms) of each kernel of one fa_bwd launch in the
+    committed kernel-trace summary of the default workload, or None."""
+    text = _profile_text(KERNELS_FILE)
+    if text is None:
+        return None
+    names = (["dkdv_q2_kernel<128, false>", "dq_kernel<128, false>"] if mode == "deterministic"
+             else ["dkdv_atomic_kernel<128>", "dq_convert_kernel"])
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip().strip("`") for c in line.split("|")]
+        if len(cells) > 4:
+            for n in names:
+                if cells[1].startswith(n):
+                    out[n] = round(float(cells[3]) / 1000.0, 4)
+    return out if len(out) == len(names) else None
+
+
+def profiled_clock_mhz():
+    """Shader clock under the backward's load, from the committed counter run
+    (cycles over the same dispatches' durations), or None."""
+    text = _profile_text(CLOCK_FILE)
+    m = re.search(r"clock_mhz_under_load:\s*([0-9.]+)", text or "")
+    return float(m.group(1)) if m else None
+
+
+def device_max_clock_mhz(torch):
+    """The peak engine clock the HIP runtime reports for device 0 (MHz)."""
+    try:
+        lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        val = ctypes.c_int(0)
+        if lib.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0:  # hipDeviceAttributeClockRate (kHz)
+            return val.value / 1000.0
+    except OSError:
+        pass
+    return None
 
 
 def device_info(torch, dev):
@@ -311,6 +362,21 @@ def main():
                        "value": round(flops / (other_run["ms_per_step"] * 1e-3) / 1e12, 2)},
         "device": device_info(torch, dev),
     }
+    # The peak above is quoted at 2.4 GHz; under this load the shader clock
+    # runs lower.  The device's reported peak clock, the clock the committed
+    # counter run measured on these kernels, and the peak at that clock.
+    max_mhz = device_max_clock_mhz(torch)
+    load_mhz = profiled_clock_mhz() if w.name == "train_causal_bf16" else None
+    line["clock"] = {"device_max_mhz": max_mhz, "under_load_mhz": load_mhz,
+                     "source": CLOCK_FILE if load_mhz else None}
+    if load_mhz:
+        peak_clk = PEAK_BF16_TFLOPS * load_mhz / PEAK_CLOCK_MHZ
+        line["roofline_at_clock"] = {"peak": round(peak_clk, 1), "achieved": round(achieved, 2),
+                                     "frac": round(achieved / peak_clk, 4),
+                                     "value_frac": round(tflops / peak_clk, 4)}
+    split = profiled_kernel_ms(args.mode) if w.name == "train_causal_bf16" else None
+    if split:
+        line["kernels_ms_profiled"] = dict(split, source=KERNELS_FILE)
     fwd_flops = flops * 4 / 10  # forward: S and O products, 4 d per visible pair
     if fwd_ms is not None:
         line["forward"] = {"ms": round(fwd_ms, 4), "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),

@@ -11,7 +11,8 @@ High level: forward(...) and backward(...) take [B, H, N, d] torch tensors
 on the GPU (queries and keys may differ in N), forward_varlen(...) and
 backward_varlen(...) packed [total, H, d] tensors with cumulative sequence
 offsets; they allocate the outputs with torch and enqueue on torch's
-current stream.
+current stream (or on the stream passed as `stream=`, on which they then
+also allocate).
 """
 
 import ctypes
@@ -225,6 +226,16 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context in which the helpers allocate: the caller's stream when one
+    is given, so that the caching allocator ties every output and temporary
+    to the stream the kernels run on (a temporary freed on return is then
+    reused only by later work on that same stream)."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _check(status, where):
     if status != 0:
         raise FaError(status, where)
@@ -237,8 +248,9 @@ def forward(q, k, v, sm_scale=None, causal=False, window=(-1, -1), dropout_p=0.0
     _validate(q, k, v)
     params = make_params(tuple(q.shape), _dtype_code(q), sm_scale, causal, window, dropout_p,
                          seed, offset, seqlen_k=k.shape[2])
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    with _alloc_on(stream):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):  # the library launches on the current device
         _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
                       ctypes.c_void_p(lse.data_ptr()), _stream(stream, q.device)), "fa_fwd")
@@ -262,18 +274,20 @@ def backward(q, k, v, o, dout, lse, sm_scale=None, causal=False, window=(-1, -1)
 def _backward(params, q, k, v, o, dout, lse, delta_shape, stream, workspace, delta):
     import torch
     st = _stream(stream, q.device)
-    if delta is None:
-        delta = torch.empty(delta_shape, dtype=torch.float32, device=q.device)
-    else:
-        _check_f32(delta, "delta", delta_shape, q.device)
     ws_bytes = fa_bwd_workspace_bytes(params)
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device)
-    elif ws_bytes and (workspace.dtype != torch.float32 or workspace.device != q.device
-                       or not workspace.is_contiguous() or workspace.numel() * 4 < ws_bytes):
+    if delta is not None:
+        _check_f32(delta, "delta", delta_shape, q.device)
+    if ws_bytes and workspace is not None and (
+            workspace.dtype != torch.float32 or workspace.device != q.device
+            or not workspace.is_contiguous() or workspace.numel() * 4 < ws_bytes):
         raise ValueError(f"workspace must be a contiguous float32 tensor of at least {ws_bytes} bytes on {q.device}")
+    with _alloc_on(stream):
+        if delta is None:
+            delta = torch.empty(delta_shape, dtype=torch.float32, device=q.device)
+        if ws_bytes and workspace is None:
+            workspace = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if ws_bytes else ctypes.c_void_p(0)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     with torch.cuda.device(q.device):
         _check(fa_bwd_preprocess(params, tensor_arg(o), tensor_arg(dout),
                                  ctypes.c_void_p(delta.data_ptr()), ws_ptr, st), "fa_bwd_preprocess")
@@ -311,9 +325,10 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     _validate(q, k, v, varlen=True)
     params = _varlen_params(q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale,
                             causal, window, dropout_p, seed, offset)
-    o = torch.empty_like(q)
-    lse = torch.empty((params.batch, q.shape[1], params.seqlen), dtype=torch.float32,
-                      device=q.device)
+    with _alloc_on(stream):
+        o = torch.empty_like(q)
+        lse = torch.empty((params.batch, q.shape[1], params.seqlen), dtype=torch.float32,
+                          device=q.device)
     with torch.cuda.device(q.device):
         _check(fa_fwd(params, tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
                       ctypes.c_void_p(lse.data_ptr()), _stream(stream, q.device)), "fa_fwd")
@@ -344,7 +359,8 @@ def debug_dropout_mask(shape, b, h, dropout_p, seed, offset=0, device="cuda", st
     params = make_params(shape, FA_DTYPE_F32, None, False, (-1, -1), dropout_p, seed, offset,
                          seqlen_k=seqlen_k)
     n = shape[2]
-    mask = torch.empty((n, params.seqlen_k), dtype=torch.uint8, device=device)
+    with _alloc_on(stream):
+        mask = torch.empty((n, params.seqlen_k), dtype=torch.uint8, device=device)
     with torch.cuda.device(mask.device):
         _check(fa_debug_dropout_mask(params, b, h, ctypes.c_void_p(mask.data_ptr()),
                                      _stream(stream, mask.device)), "fa_debug_dropout_mask")

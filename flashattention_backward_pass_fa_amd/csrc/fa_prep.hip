@@ -2,9 +2,10 @@
 //
 //  prep_kernel        D_i = sum_k dO_ik O_ik for every row, fp32 accumulate
 //                     ("FlashAttention backward", section "The gradients, and
-//                     the one scalar that makes them local": one cheap pass
-//                     over dO and O before the main loop), fused with zeroing
-//                     the fp32 dQ accumulator of atomic mode.
+//                     the one scalar that makes them local": a single
+//                     streaming pass over O and dO ahead of the backward
+//                     kernels), fused with zeroing the fp32 dQ accumulator of
+//                     atomic mode.
 //  dq_convert_kernel  dQ = round_to_dtype(sm_scale * dQ_acc) (bf16 or fp16).
 //  mask_kernel        the dropout keep mask of one head (test aid).
 //

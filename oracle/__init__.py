@@ -28,7 +28,7 @@ from .attention import (  # noqa: F401
     dropout_mask,
     forward,
     head_backward,
-    head_delta,
+    head_columns_backward,
     head_forward,
     head_rows_backward,
     head_rows_forward,

@@ -197,9 +197,47 @@ def head_backward(q, k, v, do, spec, b=0, h=0, chunk=None):
     return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": lse, "delta": delta}
 
 
-def head_delta(o, do):
-    """D_i = rowsum(dO * O) for given O and dO of one head ([N, d] each)."""
-    return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=1)
+def head_columns_backward(q, k, v, do, spec, b, h, cols, chunk=None):
+    """dK and dV of the key rows `cols` of one head ([len(cols), d] each).
+
+    dK_j = sm_scale * sum_i dS_ij Q_i and dV_j = sum_i P~_ij dO_i, summed over
+    every query row i that sees one of the keys ("Lecture 7", section "The
+    math").  Each such row is taken whole: its L and O come from
+    head_rows_forward over its complete key row, D_i = rowsum(dO_i * O_i)
+    ("FlashAttention backward", section "The gradients, and the one scalar
+    that makes them local") and dS = P * (dP - D).  The cost is that of the
+    rows that see the keys, not of the whole head.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    cols = np.asarray(cols, dtype=np.int64)
+    nq, n = q.shape[0], k.shape[0]
+    shift = n - nq
+    seeing = np.nonzero(valid_mask(np.arange(nq), cols, spec, shift).any(axis=1))[0]
+    dk = np.zeros((len(cols), q.shape[1]))
+    dv = np.zeros((len(cols), v.shape[1]))
+    step = len(seeing) if chunk is None else max(1, int(chunk))
+    for start in range(0, len(seeing), step):
+        rows = seeing[start:start + step]
+        f = head_rows_forward(q, k, v, spec, b, h, rows)
+        ok = valid_mask(rows, cols, spec, shift) & np.isfinite(f["lse"])[:, None]
+        s = spec.sm_scale * (q[rows] @ k[cols].T)
+        p = np.zeros_like(s)
+        p[ok] = np.exp((s - np.where(ok, f["lse"][:, None], 0.0))[ok])
+        dp = do[rows] @ v[cols].T
+        if spec.dropout_p > 0.0:
+            z = philox.dropout_keep(spec.seed, spec.offset, b, h, rows, cols, spec.dropout_p)
+            p_drop = p * z / (1.0 - spec.dropout_p)
+            dp = dp * z / (1.0 - spec.dropout_p)
+        else:
+            p_drop = p
+        d_row = (do[rows] * f["o"]).sum(axis=1)
+        ds = p * (dp - d_row[:, None])
+        dk += spec.sm_scale * (ds.T @ q[rows])
+        dv += p_drop.T @ do[rows]
+    return {"dk": dk, "dv": dv}
 
 
 def forward(q, k, v, spec, heads=None, chunk=None):

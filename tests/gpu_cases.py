@@ -48,17 +48,21 @@ def errors(got, ref):
 UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 
 
-def zero_floor(name, dtype, d, scale, mags):
+def zero_floor(name, dtype, d, scale, mags, n_q=1, dropout_p=0.0):
     """Rounding-error bound for a gradient that is exactly zero in real
-    arithmetic (e.g. dQ, dK at N = 1).  There dS = P (dP - D) is the
-    difference of one dot product of length d computed two ways, so
-    |dS| <= 4 d u |dO| |V|, and dQ = scale dS K (dK = scale dS^T Q) sums
-    such terms with weights P that add up to 1."""
+    arithmetic (e.g. dQ, dK at N = 1).  There dS_ij = P_ij (dP_ij - D_i) is
+    P_ij times the difference of one dot product of length d computed two
+    ways, so |dS_ij| <= 4 d u |dO| |V| P_ij / (1 - p) (dropout scales dP and
+    D by the kept weights' 1 / (1 - p)).  dQ_i = scale sum_j dS_ij K_j sums
+    over a row of P, whose weights add up to 1; dK_j = scale sum_i dS_ij Q_i
+    sums over a column of P, whose weights add up to at most the number of
+    query rows n_q."""
     u = UNIT_ROUNDOFF[dtype]
     other = {"dq": mags["k"], "dk": mags["q"]}.get(name)
     if other is None:
         return 0.0
-    return 4.0 * d * u * abs(scale) * mags["do"] * mags["v"] * other
+    weight = 1.0 if name == "dq" else float(max(1, n_q))
+    return 4.0 * d * u * abs(scale) * mags["do"] * mags["v"] * other * weight / (1.0 - dropout_p)
 
 
 def assert_close(name, got, ref, dtype, floor=0.0):
@@ -136,7 +140,8 @@ def compare(case, gpu, ref, heads=None, names=("o", "dq", "dk", "dv"), host=None
     for name in names:
         got = sel(to_host(gpu[name]))
         want = sel(ref[name])
-        floor = zero_floor(name, case.dtype, case.shape[3], case.sm_scale, mags) if mags else 0.0
+        floor = (zero_floor(name, case.dtype, case.shape[3], case.sm_scale, mags, case.shape[2],
+                            case.dropout_p) if mags else 0.0)
         report[name] = assert_close(name, got, want, case.dtype, floor)
     got_l = sel(to_host(gpu["lse"]))
     want_l = sel(ref["lse"])

@@ -1,13 +1,16 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Small problems are compared element by element in full (they span several
-tiles and a ragged tail); the measured full-size workloads are compared on
-sampled heads, in the launch configuration the benchmark times.
+tiles and a ragged tail).  The measured full-size workloads run in the
+launch configuration the benchmark times, in both dQ modes: the training
+shape is compared on every head, the larger two on a few full heads and on
+sampled rows and keys of every head.
 """
 
 import numpy as np
 import pytest
 
+import oracle
 from tests.gpu_cases import Case, compare, to_host, assert_close
 
 pytestmark = pytest.mark.gpu
@@ -34,19 +37,74 @@ def test_small_causal_bf16(deterministic):
     _run_and_compare(Case(2, 4, 1024, 64, "bf16", causal=True, seed=1002), deterministic)
 
 
+# The three large workloads, in both dQ modes, in the launch configuration
+# the benchmark times.  The training shape is compared on every head in
+# full.  The two larger ones are compared in full on a few heads, and on
+# every head on samples the oracle can compute on their own: 16 random query
+# rows (O, L, D, dQ of those rows; head_rows_backward takes each row whole)
+# and a run of 8 consecutive keys (dK, dV of those keys, from every row that
+# sees them; head_columns_backward).  A sample meets the same bars as a whole
+# tensor, taken over the sampled values.
+FULL_SIZE = {
+    # name: (case, fully compared heads (None: all), last keys the sampled key runs start in)
+    "train_causal": (Case(4, 16, 4096, 128, "bf16", causal=True, seed=1003), None, None),
+    "window_dropout": (Case(2, 16, 8192, 64, "bf16", window=(1023, 1023), dropout_p=0.1, seed=1004),
+                       [(0, 0), (1, 13), (0, 9), (1, 4)], None),
+    # keys near the end: the rows that see them are few enough to take whole
+    "long_causal": (Case(1, 8, 32768, 128, "bf16", causal=True, seed=1005), [(0, 5), (0, 2)], 2048),
+}
+
+_oracle_cache = {}
+
+
+def _full_size_oracle(name):
+    """Inputs and oracle result of a large workload, computed once for both modes."""
+    if name not in _oracle_cache:
+        _oracle_cache.clear()  # hold one workload at a time
+        case, heads, _ = FULL_SIZE[name]
+        host = case.host_inputs()
+        _oracle_cache[name] = (host, case.run_oracle(host, heads=heads))
+    return _oracle_cache[name]
+
+
+def _sampled_rows_and_keys(case, host, gpu, key_window, seed):
+    spec = case.spec()
+    B, H, N, _ = case.shape
+    rng = np.random.default_rng(seed)
+    got = {n: to_host(gpu[n]) for n in ("o", "lse", "delta", "dq", "dk", "dv")}
+    g = {n: [] for n in got}
+    w = {n: [] for n in got}
+    for b in range(B):
+        for h in range(H):
+            args = (host["q"][b, h], host["k"][b, h], host["v"][b, h], host["do"][b, h])
+            rows = np.sort(rng.choice(N, 16, replace=False))
+            r = oracle.head_rows_backward(*args, spec, b, h, rows)
+            for n in ("o", "lse", "delta", "dq"):
+                g[n].append(got[n][b, h][rows])
+                w[n].append(r[n])
+            lo = 0 if key_window is None else N - key_window
+            j0 = int(rng.integers(lo, N - 8 + 1))
+            cols = np.arange(j0, j0 + 8)
+            c = oracle.head_columns_backward(*args, spec, b, h, cols, chunk=1024)
+            for n in ("dk", "dv"):
+                g[n].append(got[n][b, h][cols])
+                w[n].append(c[n])
+    for n in ("o", "delta", "dq", "dk", "dv"):
+        assert_close(f"sampled {n}", np.concatenate(g[n]), np.concatenate(w[n]), case.dtype)
+    lse_err = float(np.abs(np.concatenate(g["lse"]) - np.concatenate(w["lse"])).max())
+    assert lse_err <= 1e-3, f"sampled lse: max|err| {lse_err:.3e}"
+
+
 @pytest.mark.parametrize("deterministic", [False, True])
-def test_train_causal_bf16_sampled_heads(deterministic):
-    _run_and_compare(Case(4, 16, 4096, 128, "bf16", causal=True, seed=1003), deterministic,
-                     heads=[(0, 0), (3, 15), (2, 9)])
-
-
-def test_window_dropout_bf16_sampled_heads():
-    _run_and_compare(Case(2, 16, 8192, 64, "bf16", window=(1023, 1023), dropout_p=0.1, seed=1004),
-                     heads=[(0, 0), (1, 13)])
-
-
-def test_long_causal_bf16_sampled_head():
-    _run_and_compare(Case(1, 8, 32768, 128, "bf16", causal=True, seed=1005), heads=[(0, 5)])
+@pytest.mark.parametrize("name", list(FULL_SIZE))
+def test_full_size_workload(name, deterministic):
+    case, heads, key_window = FULL_SIZE[name]
+    print(f"\n[gpu] {name}: {case} deterministic={deterministic} heads={heads or 'all'}", flush=True)
+    host, ref = _full_size_oracle(name)
+    gpu = case.run_gpu(case.device_inputs(host), deterministic=deterministic)
+    compare(case, gpu, ref, heads=heads, names=("o", "delta", "dq", "dk", "dv"), host=host)
+    if heads is not None:
+        _sampled_rows_and_keys(case, host, gpu, key_window, seed=case.seed + 17 * deterministic)
 
 
 # ------------------------------------------- ragged shapes and every flag

@@ -71,7 +71,8 @@ def test_unequal_lengths(B, H, Nq, Nk, d, dtype, causal, window, p, deterministi
     ref = oracle.backward(host["q"], host["k"], host["v"], host["do"], spec)
     mags = {n: float(np.abs(host[n]).max()) for n in ("q", "k", "v", "do")}
     for name, got in (("o", o), ("delta", delta), ("dq", dq), ("dk", dk), ("dv", dv)):
-        assert_close(name, to_host(got), ref[name], dtype, zero_floor(name, dtype, d, spec.sm_scale, mags))
+        assert_close(name, to_host(got), ref[name], dtype,
+                     zero_floor(name, dtype, d, spec.sm_scale, mags, Nq, p))
     _check_lse(to_host(lse), ref["lse"])
     if causal and Nq > Nk and window[0] < 0:
         empty = Nq - Nk
@@ -112,7 +113,8 @@ def test_varlen(lq, lk, H, d, dtype, causal, window, p, deterministic):
     ref = oracle.varlen_backward(host["q"], host["k"], host["v"], host["do"], cu_q, cu_k, spec)
     mags = {n: float(np.abs(host[n]).max()) for n in ("q", "k", "v", "do")}
     for name, got in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
-        assert_close(name, to_host(got), ref[name], dtype, zero_floor(name, dtype, d, spec.sm_scale, mags))
+        assert_close(name, to_host(got), ref[name], dtype,
+                     zero_floor(name, dtype, d, spec.sm_scale, mags, mq, p))
     valid = ~np.isnan(ref["lse"])
     _check_lse(to_host(lse)[valid], ref["lse"][valid])
     assert_close("delta", to_host(delta)[valid], ref["delta"][valid], dtype)

@@ -12,7 +12,9 @@ import pytest
 import oracle
 from flashattention_backward_pass_fa_amd import binding as fa
 from flashattention_backward_pass_fa_amd.inputs import cumulative, make_tensors
-from tests.gpu_cases import assert_close, to_device, to_host, zero_floor
+from tests.gpu_cases import (TOL_BF16_FRO, TOL_BF16_MAX, assert_close, errors, to_device, to_host,
+                             zero_floor)
+from tests.rounding_cases import KNOWN, model_case
 
 pytestmark = pytest.mark.gpu
 
@@ -21,9 +23,9 @@ N_CASES = 80
 # 491, a 3-row dropout problem whose single-key row must give dQ = 0 (the
 # kept weight was rounded with its 1 / (1 - p) factor, biasing D)
 REGRESSIONS = [491]
-# Configurations of that run whose bars the method's own bf16 rounding already
-# misses (single-key rows, near-cancelling D) are checked on the CPU instead,
-# against a model of that rounding: tests/test_oracle_rounding_floor.py.
+# Configurations whose bars the method's own bf16 rounding already misses
+# (single-key rows, near-cancelling D) are tests/rounding_cases.py's KNOWN:
+# test_rounding_limited_configuration below runs each of them here.
 
 
 def _draw(i):
@@ -66,13 +68,10 @@ def _kw(spec):
                 seed=spec.seed, offset=spec.offset)
 
 
-@pytest.mark.parametrize("i", list(range(N_CASES)) + REGRESSIONS)
-def test_random_configuration(i):
+def run_configuration(c, spec):
+    """GPU forward and backward of configuration c through the C ABI, and
+    the oracle's result; returns (gpu outputs on the host, oracle, magnitudes)."""
     import torch
-    c = _draw(i)
-    print(f"\n[gpu] sweep {i}: {c}", flush=True)
-    spec = oracle.Spec(sm_scale=c["scale"], causal=c["causal"], window_left=c["window"][0],
-                       window_right=c["window"][1], dropout_p=c["p"], seed=77 + i, offset=i)
     H, d, dtype = c["H"], c["d"], c["dtype"]
     if c["varlen"]:
         cu_q, cu_k = cumulative(c["lq"]), cumulative(c["lk"])
@@ -97,14 +96,64 @@ def test_random_configuration(i):
                                         deterministic=c["det"], **_kw(spec))
         ref = oracle.backward(host["q"], host["k"], host["v"], host["do"], spec)
     torch.cuda.synchronize()
+    got = {n: to_host(t) for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv),
+                                      ("delta", delta))}
     mags = {n: float(np.abs(host[n]).max()) if host[n].size else 0.0 for n in ("q", "k", "v", "do")}
-    for name, got in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
-        assert_close(name, to_host(got), ref[name], dtype,
-                     zero_floor(name, dtype, d, spec.sm_scale, mags))
-    want_l, got_l = ref["lse"], to_host(lse)
+    return got, ref, mags
+
+
+def _query_rows(c):
+    return max(c["lq"]) if c["varlen"] else c["Nq"]
+
+
+def check_lse(got_l, want_l):
     valid = ~np.isnan(want_l)
     assert np.array_equal(np.isneginf(got_l[valid]), np.isneginf(want_l[valid]))
     live = valid & np.isfinite(want_l)
     if live.any():
         assert float(np.abs(got_l[live] - want_l[live]).max()) <= 1e-3
-    assert_close("delta", to_host(delta)[valid], ref["delta"][valid], dtype)
+    return valid
+
+
+@pytest.mark.parametrize("i", list(range(N_CASES)) + REGRESSIONS)
+def test_random_configuration(i):
+    c = _draw(i)
+    print(f"\n[gpu] sweep {i}: {c}", flush=True)
+    spec = oracle.Spec(sm_scale=c["scale"], causal=c["causal"], window_left=c["window"][0],
+                       window_right=c["window"][1], dropout_p=c["p"], seed=77 + i, offset=i)
+    got, ref, mags = run_configuration(c, spec)
+    for name in ("o", "dq", "dk", "dv"):
+        assert_close(name, got[name], ref[name], c["dtype"],
+                     zero_floor(name, c["dtype"], c["d"], spec.sm_scale, mags, _query_rows(c), c["p"]))
+    valid = check_lse(got["lse"], ref["lse"])
+    assert_close("delta", got["delta"][valid], ref["delta"][valid], c["dtype"])
+
+
+@pytest.mark.parametrize("i,c,name,reading", KNOWN, ids=[str(k[0]) for k in KNOWN])
+def test_rounding_limited_configuration(i, c, name, reading):
+    """A configuration whose `name` tensor the method's own bf16 rounding
+    takes past the whole-tensor bar: every other tensor meets the bars, and
+    `name` stays within 1.1 times the rounding model's error (max and
+    relative Frobenius, each bounded by the larger of the bar and that)."""
+    print(f"\n[gpu] rounding-limited {i} ({name} {reading}): {c}", flush=True)
+    spec, _, ref_m, model, mags = model_case(c, i)
+    got, ref, _ = run_configuration(c, spec)
+    valid = check_lse(got["lse"], ref["lse"])
+    sel = {"delta": valid}
+    for n in ("o", "dq", "dk", "dv", "delta"):
+        g = got[n][sel[n]] if n in sel else got[n]
+        r = ref[n][sel[n]] if n in sel else ref[n]
+        if n != name:
+            assert_close(n, g, r, c["dtype"],
+                         zero_floor(n, c["dtype"], c["d"], spec.sm_scale, mags, _query_rows(c), c["p"]))
+            continue
+        m = model[n][sel[n]] if n in sel else model[n]
+        g_max, r_max, g_fro = errors(g, r)
+        m_max, _, m_fro = errors(m, r)
+        bar_max = TOL_BF16_MAX * r_max
+        assert g_max <= max(bar_max, 1.1 * m_max), (
+            f"{n}: max|err| {g_max:.4e} > max(bar {bar_max:.4e}, 1.1 x model {m_max:.4e})")
+        assert g_fro <= max(TOL_BF16_FRO, 1.1 * m_fro), (
+            f"{n}: rel Frobenius {g_fro:.4e} > max(bar {TOL_BF16_FRO}, 1.1 x model {m_fro:.4e})")
+        print(f"[gpu] {n}: max|err| {g_max:.4e} (model {m_max:.4e}), rel Frobenius {g_fro:.4e} "
+              f"(model {m_fro:.4e})", flush=True)

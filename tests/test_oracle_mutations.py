@@ -42,6 +42,18 @@ UNEQUAL_MUTANTS = {
 }
 
 
+# Mistakes in the selected-key-columns backward
+COLUMN_MUTANTS = {
+    "columns_only_rows_seeing_all": (".any(axis=1))[0]", ".all(axis=1))[0]"),
+    "columns_dv_without_dropout": ("dv += p_drop.T @ do[rows]", "dv += p.T @ do[rows]"),
+    "columns_dp_without_dropout": ("dp = dp * z / (1.0 - spec.dropout_p)", "dp = dp * z"),
+    "columns_unscaled_dk": ("dk += spec.sm_scale * (ds.T @ q[rows])", "dk += (ds.T @ q[rows])"),
+    # D from the selected keys only instead of the whole row
+    "columns_local_D": ("d_row = (do[rows] * f[\"o\"]).sum(axis=1)\n        ds",
+                        "d_row = (p * dp).sum(axis=1)\n        ds"),
+}
+
+
 def _load_mutant(old, new):
     src = inspect.getsource(attention)
     assert old in src, old
@@ -123,9 +135,45 @@ def _unequal_pins_pass(mod):
     return True
 
 
+def _columns_pins_pass(mod):
+    """A compact run of the key-columns pin: torch autograd columns of dK, dV."""
+    rng = np.random.default_rng(13)
+    n, d = 30, 6
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    cols = np.array([0, 3, 17, 29])
+    for kw in ({"causal": True}, {"window_left": 4, "window_right": 2, "dropout_p": 0.3, "seed": 8}):
+        sp = mod.Spec(sm_scale=0.7, **kw)
+        r = mod.head_columns_backward(q, k, v, do, sp, 0, 0, cols, chunk=7)
+        i = torch.arange(n).view(-1, 1)
+        j = torch.arange(n).view(1, -1)
+        ok = torch.ones(n, n, dtype=torch.bool)
+        if sp.causal:
+            ok &= j <= i
+        if sp.window_left >= 0:
+            ok &= (j >= i - sp.window_left) & (j <= i + sp.window_right)
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        p = torch.softmax(((tq @ tk.T) * sp.sm_scale).masked_fill(~ok, float("-inf")), -1)
+        if sp.dropout_p > 0:
+            z = torch.tensor(oracle.dropout_keep(sp.seed, sp.offset, 0, 0, np.arange(n),
+                                                 np.arange(n), sp.dropout_p), dtype=torch.float64)
+            p = p * z / (1 - sp.dropout_p)
+        (p @ tv).backward(torch.tensor(do))
+        for name, t in (("dk", tk), ("dv", tv)):
+            if not np.allclose(r[name], t.grad.numpy()[cols], rtol=1e-9, atol=1e-10):
+                return False
+    return True
+
+
 def test_unmutated_oracle_passes_compact_pins():
     assert _pins_pass(_load_mutant("", ""))
     assert _unequal_pins_pass(_load_mutant("", ""))
+    assert _columns_pins_pass(_load_mutant("", ""))
+
+
+@pytest.mark.parametrize("name", list(COLUMN_MUTANTS))
+def test_column_mutant_is_caught(name):
+    old, new = COLUMN_MUTANTS[name]
+    assert not _columns_pins_pass(_load_mutant(old, new)), name
 
 
 @pytest.mark.parametrize("name", list(UNEQUAL_MUTANTS))

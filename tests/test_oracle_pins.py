@@ -347,3 +347,29 @@ def test_closed_form_credited_flops_matches_enumeration_unequal_lengths():
         spec = oracle.Spec(sm_scale=1.0, causal=causal, window_left=wl, window_right=wr)
         assert (credited_flops(2, 3, n, 16, causal, wl, wr, n_k=n_k)
                 == oracle.credited_flops(2, 3, n, 16, spec, n_k=n_k))
+
+
+# ----------------------------------------------- selected key columns only
+
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("p", [0.0, 0.3])
+def test_key_columns_match_torch_autograd(mask, p):
+    """dK, dV of a few keys, from only the rows that see them, against
+    torch fp64 autograd of the whole problem (with the oracle's keep mask
+    fixed when p > 0)."""
+    rng = np.random.default_rng(31 + int(10 * p))
+    n, d = 41, 6
+    q, k, v, do = (_rand(rng, n, d) for _ in range(4))
+    spec = _spec(d, mask, sm_scale=0.43, dropout_p=p, seed=0x5EED, offset=2)
+    cols = np.array([0, 5, 6, 23, 40])
+    r = oracle.head_columns_backward(q, k, v, do, spec, 1, 3, cols, chunk=7)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    if p > 0:
+        z = torch.from_numpy(oracle.dropout_keep(spec.seed, spec.offset, 1, 3, np.arange(n),
+                                                 np.arange(n), p).astype(np.float64))
+        o = _torch_explicit_dropout(tq, tk, tv, spec, z)
+    else:
+        o = _torch_sdpa(tq, tk, tv, spec)
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(r["dk"], tk.grad.numpy()[cols], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(r["dv"], tv.grad.numpy()[cols], rtol=1e-10, atol=1e-11)

@@ -236,3 +236,23 @@ def test_credited_flops_count_unequal_visible_pairs():
     assert oracle.credited_flops(1, 1, 3, 2, spec, n_k=8) == 10 * 2 * (6 + 7 + 8)
     # nq = 8 queries over 3 keys: rows 5, 6, 7 see 1, 2, 3 keys
     assert oracle.credited_flops(1, 1, 8, 2, spec, n_k=3) == 10 * 2 * (1 + 2 + 3)
+
+
+@pytest.mark.parametrize("nq,nk", SHAPES)
+def test_key_columns_lower_right_causal_match_torch(nq, nk):
+    """dK, dV of selected keys from the rows that see them, with the last
+    query aligned to the last key, against torch's lower-right causal bias."""
+    rng = np.random.default_rng(nq * 37 + nk)
+    d = 5
+    q, do = _rand(rng, nq, d), _rand(rng, nq, d)
+    k, v = _rand(rng, nk, d), _rand(rng, nk, d)
+    spec = oracle.Spec(sm_scale=0.6, causal=True)
+    cols = np.unique(np.array([0, nk // 2, nk - 1]))
+    r = oracle.head_columns_backward(q, k, v, do, spec, 0, 0, cols, chunk=3)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.view(1, 1, nq, d), tk.view(1, 1, nk, d), tv.view(1, 1, nk, d),
+        attn_mask=_lower_right(nq, nk), scale=0.6).view(nq, d)
+    o.backward(torch.tensor(do))
+    np.testing.assert_allclose(r["dk"], tk.grad.numpy()[cols], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(r["dv"], tv.grad.numpy()[cols], rtol=1e-9, atol=1e-11)
