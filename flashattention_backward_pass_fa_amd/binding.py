@@ -5,7 +5,7 @@ in the library's HIP kernels.  The library is loaded on first use from this
 package directory; if it is missing the call raises (there is no fallback).
 
 Low level: fa_abi_version, fa_status_string, fa_fwd, fa_bwd_preprocess,
-fa_bwd_workspace_bytes, fa_bwd, fa_debug_dropout_mask take FaParams /
+fa_bwd_workspace_bytes, fa_bwd, fa_bwd_noalloc, fa_debug_dropout_mask take FaParams /
 FaTensor structures and raw device pointers, exactly like the C functions.
 High level: forward(...) and backward(...) take [B, H, N, d] torch tensors
 on the GPU (queries and keys may differ in N), forward_varlen(...) and
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F16 = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS_NAMES = {
     0: "FA_SUCCESS",
@@ -34,10 +34,13 @@ STATUS_NAMES = {
     3: "FA_ERR_MISALIGNED",
     4: "FA_ERR_LAUNCH_FAILED",
     5: "FA_ERR_HIP",
+    6: "FA_ERR_TOO_LARGE",
 }
 
+STATIC_WORKSPACE_BYTES = 128 * 1024 * 1024  # FA_STATIC_WORKSPACE_BYTES
+
 EXPORTS = ("fa_abi_version", "fa_last_hip_error", "fa_status_string", "fa_fwd", "fa_bwd_preprocess",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_debug_dropout_mask")
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_noalloc", "fa_debug_dropout_mask")
 
 
 class FaTensor(ctypes.Structure):
@@ -95,6 +98,8 @@ def load_library(path=LIB_PATH):
     lib.fa_bwd_workspace_bytes.argtypes = [P]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [P, T, T, T, T, fp, fp, T, T, T, fp, vp]
+    lib.fa_bwd_noalloc.restype = ctypes.c_int
+    lib.fa_bwd_noalloc.argtypes = [P, T, T, T, T, fp, fp, T, T, T, vp]
     lib.fa_debug_dropout_mask.restype = ctypes.c_int
     lib.fa_debug_dropout_mask.argtypes = [P, ctypes.c_int32, ctypes.c_int32, vp, vp]
     if lib.fa_abi_version() != ABI_VERSION:
@@ -132,6 +137,11 @@ def fa_bwd_workspace_bytes(params):
 def fa_bwd(params, q, k, v, dout, lse, delta, dq, dk, dv, dq_acc, stream):
     return load_library().fa_bwd(ctypes.byref(params), q, k, v, dout, lse, delta, dq, dk, dv,
                                  dq_acc, stream)
+
+
+def fa_bwd_noalloc(params, q, k, v, dout, lse, delta, dq, dk, dv, stream):
+    return load_library().fa_bwd_noalloc(ctypes.byref(params), q, k, v, dout, lse, delta, dq, dk, dv,
+                                         stream)
 
 
 def fa_debug_dropout_mask(params, b, h, mask, stream):

@@ -25,6 +25,7 @@ ARCH = "gfx950"
 SOURCES = [
     ("fa_api.cpp", [], "fa_api"),
     ("fa_prep.hip", [], "fa_prep"),
+    ("fa_noalloc.hip", [], "fa_noalloc"),
     ("fa_f32.hip", [], "fa_f32"),
     ("fa_fwd16.hip", [], "fa_fwd16_bf16"),
     ("fa_bwd16.hip", [], "fa_bwd16_bf16"),

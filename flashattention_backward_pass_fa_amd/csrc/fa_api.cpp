@@ -10,6 +10,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 #include <initializer_list>
 
 #include "../../include/fa.h"
@@ -172,6 +173,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_MISALIGNED: return "pointer or stride misaligned";
     case FA_ERR_LAUNCH_FAILED: return "kernel launch failed";
     case FA_ERR_HIP: return "HIP runtime error (no usable device?)";
+    case FA_ERR_TOO_LARGE: return "dQ workspace larger than FA_STATIC_WORKSPACE_BYTES";
   }
   return "unknown status";
 }
@@ -237,8 +239,14 @@ fa_status fa_bwd_preprocess(const fa_params* p, fa_tensor o, fa_tensor dout, flo
   return launched(fa::launch_preprocess(a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor dout, const float* lse,
-                 const float* delta, fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of fa_bwd except the workspace's.
+fa_status check_bwd(const fa_params* p, const fa_tensor& q, const fa_tensor& k, const fa_tensor& v,
+                    const fa_tensor& dout, const float* lse, const float* delta, const fa_tensor& dq,
+                    const fa_tensor& dk, const fa_tensor& dv) {
   FA_TRY(check_params(p));
   FA_TRY(check_tensor(p, q));
   FA_TRY(check_tensor(p, k));
@@ -249,12 +257,17 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   FA_TRY(check_tensor(p, dv));
   FA_TRY(check_vec(lse, 4));
   FA_TRY(check_vec(delta, 4));
-  const bool atomic = uses_dq_acc(p);
-  if (atomic) FA_TRY(check_vec(dq_acc, 16));
-  if (aliased(p, {dq.ptr, dk.ptr, dv.ptr, atomic ? dq_acc : nullptr},
-              {q.ptr, k.ptr, v.ptr, dout.ptr, lse, delta}))
+  if (aliased(p, {dq.ptr, dk.ptr, dv.ptr}, {q.ptr, k.ptr, v.ptr, dout.ptr, lse, delta}))
     return FA_ERR_INVALID_VALUE;
-  FA_TRY(device_ready());
+  return FA_SUCCESS;
+}
+
+// The launches of fa_bwd, after validation; dq_acc is the (zeroed) fp32
+// workspace in atomic mode, else ignored.
+fa_status run_bwd(const fa_params* p, const fa_tensor& q, const fa_tensor& k, const fa_tensor& v,
+                  const fa_tensor& dout, const float* lse, const float* delta, const fa_tensor& dq,
+                  const fa_tensor& dk, const fa_tensor& dv, float* dq_acc, hipStream_t s) {
+  const bool atomic = uses_dq_acc(p);
   fa::BwdArgs a{};
   a.q = view(p, q);
   a.k = view(p, k);
@@ -273,7 +286,6 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
   a.sm_scale = p->sm_scale;
   a.scale_log2 = p->sm_scale * kLog2e;
   a.m = mask_args(p);
-  hipStream_t s = (hipStream_t)stream;
   if (p->dtype == FA_DTYPE_F32) return launched(fa::launch_bwd_f32(a, s));
   FA_TRY(launched(p->dtype == FA_DTYPE_F16 ? fa::fp16::launch_bwd16(a, !atomic, s)
                                              : fa::launch_bwd16(a, !atomic, s)));
@@ -291,6 +303,44 @@ fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_t
     FA_TRY(launched(fa::launch_dq_convert(c, s)));
   }
   return FA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor dout, const float* lse,
+                 const float* delta, fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc, void* stream) {
+  FA_TRY(check_bwd(p, q, k, v, dout, lse, delta, dq, dk, dv));
+  const bool atomic = uses_dq_acc(p);
+  if (atomic) {
+    FA_TRY(check_vec(dq_acc, 16));
+    if (aliased(p, {dq_acc}, {q.ptr, k.ptr, v.ptr, dout.ptr, lse, delta, dq.ptr, dk.ptr, dv.ptr}))
+      return FA_ERR_INVALID_VALUE;
+  }
+  FA_TRY(device_ready());
+  return run_bwd(p, q, k, v, dout, lse, delta, dq, dk, dv, dq_acc, (hipStream_t)stream);
+}
+
+fa_status fa_bwd_noalloc(const fa_params* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor dout,
+                         const float* lse, const float* delta, fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                         void* stream) {
+  FA_TRY(check_bwd(p, q, k, v, dout, lse, delta, dq, dk, dv));
+  const size_t ws = fa_bwd_workspace_bytes(p);
+  if (ws > FA_STATIC_WORKSPACE_BYTES) return FA_ERR_TOO_LARGE;
+  FA_TRY(device_ready());
+  hipStream_t s = (hipStream_t)stream;
+  float* scratch = nullptr;
+  if (ws) {
+    // this device's copy of the static array, then clear the part in use
+    const hipError_t e = fa::static_workspace(&scratch);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return FA_ERR_HIP;
+    }
+    FA_TRY(launched(fa::launch_zero(scratch, ws, s)));
+  }
+  return run_bwd(p, q, k, v, dout, lse, delta, dq, dk, dv, scratch, s);
 }
 
 fa_status fa_debug_dropout_mask(const fa_params* p, int32_t b, int32_t h, uint8_t* mask, void* stream) {

@@ -57,4 +57,10 @@ hipError_t launch_preprocess(const PrepArgs& a, hipStream_t s);
 hipError_t launch_dq_convert(const PrepArgs& a, hipStream_t s);
 hipError_t launch_dropout_mask(const MaskArgs& m, int b, int h, uint8_t* out, hipStream_t s);
 
+// The static fp32 workspace of fa_bwd_noalloc (fa_noalloc.hip): its device
+// address on the current device (looked up once per device), and a kernel
+// that zeroes the first `bytes` (a multiple of 16) of a buffer.
+hipError_t static_workspace(float** out);
+hipError_t launch_zero(float* p, size_t bytes, hipStream_t s);
+
 }  // namespace fa

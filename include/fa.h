@@ -33,8 +33,9 @@
  *     dQ = 0.
  *   - Ownership: the caller allocates every buffer (device memory) and keeps
  *     it alive until the work on `stream` completes.  The library allocates
- *     no device memory, keeps no pointer after a call returns and holds no
- *     mutable global state; calls are re-entrant.
+ *     no device memory and keeps no caller pointer after a call returns;
+ *     calls are re-entrant.  Its only global state is fa_bwd_noalloc's static
+ *     workspace (see there) and the per-device address of it.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
  *     default stream) and the call returns after launch.  Kernels run on the
  *     calling thread's current HIP device: the buffers and `stream` must
@@ -60,7 +61,10 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
+
+/* Size of the static device workspace of fa_bwd_noalloc (per GPU). */
+#define FA_STATIC_WORKSPACE_BYTES (128u * 1024u * 1024u)
 
 typedef enum fa_status {
   FA_SUCCESS = 0,
@@ -68,7 +72,9 @@ typedef enum fa_status {
   FA_ERR_NOT_SUPPORTED = 2,  /* valid but not implemented (dtype, head dim) */
   FA_ERR_MISALIGNED = 3,     /* pointer or stride alignment */
   FA_ERR_LAUNCH_FAILED = 4,  /* a kernel launch was rejected */
-  FA_ERR_HIP = 5             /* another HIP runtime error (e.g. no device) */
+  FA_ERR_HIP = 5,            /* another HIP runtime error (e.g. no device) */
+  FA_ERR_TOO_LARGE = 6       /* fa_bwd_noalloc: the problem's workspace exceeds
+                                FA_STATIC_WORKSPACE_BYTES */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -190,6 +196,26 @@ fa_status fa_bwd(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor dout, const float* lse, const float* delta,
                  fa_tensor dq, fa_tensor dk, fa_tensor dv, float* dq_acc,
                  void* stream);
+
+/* fa_bwd without the caller's workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments as fa_bwd except
+ * dq_acc, the same results.  Where fa_bwd needs its fp32 dQ workspace
+ * (fa_bwd_workspace_bytes(params) != 0: bf16/fp16 with deterministic == 0),
+ * this call uses a static device array of FA_STATIC_WORKSPACE_BYTES that the
+ * library holds on every GPU it runs on until the process ends, and clears
+ * the part it uses with a kernel on `stream` first; a larger workspace
+ * returns FA_ERR_TOO_LARGE before any HIP call.  Every other params needs no
+ * workspace and runs exactly as fa_bwd.  D comes from fa_bwd_preprocess as
+ * for fa_bwd (its dq_acc may be NULL).  The call allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine; its first call on a
+ * device looks up that device's array once.  All calls on one GPU share that
+ * GPU's array, so calls that overlap on one GPU (on different streams, or
+ * from several threads without ordering) race and give wrong dQ; order them
+ * on one stream. */
+fa_status fa_bwd_noalloc(const fa_params* params, fa_tensor q, fa_tensor k, fa_tensor v,
+                         fa_tensor dout, const float* lse, const float* delta,
+                         fa_tensor dq, fa_tensor dk, fa_tensor dv, void* stream);
 
 /* Test aid, O(Nq Nk) by design: writes the Nq x Nk keep mask Z (1 = kept,
  * 0 = dropped; row i = query, column j = key) of head (b, h) to device

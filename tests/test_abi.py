@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert fa.fa_abi_version() == fa.ABI_VERSION == 2
-    for code in range(6):
+    assert fa.fa_abi_version() == fa.ABI_VERSION == 3
+    for code in range(7):
         s = fa.fa_status_string(code)
         assert isinstance(s, str) and s
     assert fa.fa_status_string(99) == "unknown status"
@@ -193,3 +193,36 @@ def test_valid_call_without_device_reports_hip_error(lib):
     p = _params(deterministic=True)
     good = [_t(0x100000 * (i + 1)) for i in range(7)]
     assert fa.fa_bwd(p, *good[:4], VOID(0x900000), VOID(0xA00000), *good[4:], VOID(0), VOID(0)) == 5
+
+
+def test_noalloc_validation(lib):
+    """fa_bwd_noalloc checks what fa_bwd checks, and rejects a problem whose
+    atomic-mode workspace exceeds the static array, before any HIP call."""
+    good = [_t(0x100000 * (i + 1)) for i in range(7)]
+    lse, delta = VOID(0x900000), VOID(0xA00000)
+    # 4 * B * H * seqlen * d bytes: 4 * 8 * 32 * 1024 * 128 = 128 MiB fits, one more head does not
+    fits = _params(shape=(8, 32, 1024, 128))
+    assert fa.fa_bwd_workspace_bytes(fits) == fa.STATIC_WORKSPACE_BYTES
+    over = _params(shape=(8, 33, 1024, 128))
+    assert fa.fa_bwd_workspace_bytes(over) > fa.STATIC_WORKSPACE_BYTES
+    assert fa.fa_bwd_noalloc(over, *good[:4], lse, delta, *good[4:], VOID(0)) == 6
+    assert fa.fa_status_string(6) == "dQ workspace larger than FA_STATIC_WORKSPACE_BYTES"
+    # deterministic mode needs no workspace: any size passes that check
+    det = _params(shape=(8, 33, 1024, 128), deterministic=True)
+    assert fa.fa_bwd_workspace_bytes(det) == 0
+    # the same argument checks as fa_bwd
+    args = list(good)
+    args[0] = _t(0)
+    assert fa.fa_bwd_noalloc(fits, *args[:4], lse, delta, *args[4:], VOID(0)) == 1
+    assert fa.fa_bwd_noalloc(fits, *good[:4], VOID(0), delta, *good[4:], VOID(0)) == 1
+    args = list(good)
+    args[4] = good[0]
+    assert fa.fa_bwd_noalloc(fits, *args[:4], lse, delta, *args[4:], VOID(0)) == 1
+    assert fa.fa_bwd_noalloc(_params(dtype=9), *good[:4], lse, delta, *good[4:], VOID(0)) == 2
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device path; needs a host without a GPU")
+def test_noalloc_without_device_reports_hip_error(lib):
+    p = _params()
+    good = [_t(0x100000 * (i + 1)) for i in range(7)]
+    assert fa.fa_bwd_noalloc(p, *good[:4], VOID(0x900000), VOID(0xA00000), *good[4:], VOID(0)) == 5

@@ -21,7 +21,7 @@ int main(void) {
   entry_fn entry[] = {(entry_fn)fa_abi_version, (entry_fn)fa_last_hip_error,
                       (entry_fn)fa_status_string, (entry_fn)fa_fwd, (entry_fn)fa_bwd_preprocess,
                       (entry_fn)fa_bwd_workspace_bytes, (entry_fn)fa_bwd,
-                      (entry_fn)fa_debug_dropout_mask};
+                      (entry_fn)fa_bwd_noalloc, (entry_fn)fa_debug_dropout_mask};
   fa_params p = {0};
   fa_tensor t = {0, 0, 0, 0};
   (void)t;
