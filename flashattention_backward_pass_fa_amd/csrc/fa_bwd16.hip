@@ -4,8 +4,9 @@
 // The backward as a KV-outer and a Q-outer pass ("FlashAttention backward",
 // section "The loop structure"):
 //
-//  dkdv_q2_kernel  KV-outer (deterministic mode): one workgroup owns 128
-//                  keys of one (b, h) and loops over the 64-query blocks
+//  dkdv_q2_kernel  KV-outer (deterministic mode, d = 64; d = 128 uses the
+//                  producer/consumer kernel of fa_kv128.hip): one workgroup
+//                  owns 128 keys of one (b, h) and loops over the 64-query blocks
 //                  that can see them, with 8 waves (two per SIMD): 4 key
 //                  groups x 2 query halves, K and V in LDS.  For each block
 //                  it recomputes S = Q K^T and dP = dO V^T on MFMA, rebuilds
@@ -38,13 +39,11 @@
 
 #include <type_traits>
 
-#include "fa_kernels.h"
+#include "fa_bwd_common.h"
 
 namespace fa {
 FA_ELEM_NS_BEGIN
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct KvCfg {
@@ -59,51 +58,6 @@ struct KvCfg {
   static constexpr int LOADS = BR * CH / NT;
 };
 
-
-
-__device__ __forceinline__ e16x8 load8(const e16* p) { return *(const e16x8*)p; }
-__device__ __forceinline__ void store8(e16* p, e16x8 v) { *(e16x8*)p = v; }
-
-__device__ __forceinline__ e16x8 zero8() {
-  e16x8 z;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (e16)0.0f;
-  return z;
-}
-
-// The KV-outer kernels read rows past a sequence's end as copies of its
-// last row (a clamped index) rather than under a condition: a load under a
-// condition compiles to a branch that waits for it, which turned their
-// prologues into one memory round trip per load.  The copies are finite and
-// every use of them is masked or lands in rows that are never stored.  (The
-// Q-outer kernel keeps zero rows: its clamped form measured slower.)
-
-// Is every (query, key) of rows [q0, q0+rows) x keys [k0, k0+cols) visible?
-__device__ __forceinline__ bool block_full(const MaskArgs& m, int q0, int rows, int k0, int cols) {
-  return (q0 + rows <= m.nq) & (k0 + cols <= m.nk) & (k0 >= q0 + rows - 1 - m.lo_off) &
-         (k0 + cols - 1 <= q0 + m.hi_off);
-}
-
-// Is every (query, key) of that block hidden?
-__device__ __forceinline__ bool block_dead(const MaskArgs& m, int q0, int rows, int k0, int cols) {
-  return (q0 >= m.nq) | (k0 >= m.nk) | (k0 + cols - 1 < q0 - m.lo_off) |
-         (k0 > q0 + rows - 1 + m.hi_off);
-}
-
-// Specialise the call to sequence b (its lengths, mask offsets and, for
-// varlen, the packed rows it starts at).
-__device__ __forceinline__ void bwd_localize(BwdArgs& a, int b) {
-  const SeqRows r = seq_localize(a.m, b);
-  if (a.m.cu_q) {
-    shift_rows<e16>(a.q, r.q0);
-    shift_rows<e16>(a.dout, r.q0);
-    shift_rows<e16>(a.dq, r.q0);
-    shift_rows<e16>(a.k, r.k0);
-    shift_rows<e16>(a.v, r.k0);
-    shift_rows<e16>(a.dk, r.k0);
-    shift_rows<e16>(a.dv, r.k0);
-  }
-}
 
 // Elementwise step of one 32x32 S/dP accumulator pair of the KV-outer kernel:
 // P = exp2(S * c - L2), masked, dropout, dS = P (dP - D).  Writes the 16-bit
@@ -983,10 +937,15 @@ hipError_t launch_d(const BwdArgs& a, bool deterministic, hipStream_t s) {
     }
   }
   if (deterministic) {
-    hipLaunchKernelGGL(a.m.dropout ? (dkdv_q2_kernel<D, true>) : (dkdv_q2_kernel<D, false>), grid_kv,
-                       dim3(512), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if constexpr (D == 128) {
+      const hipError_t e = ::fa::FA_ELEM_NS launch_kv128(a, s);  // qualified: BwdArgs brings fa:: in by ADL
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(a.m.dropout ? (dkdv_q2_kernel<D, true>) : (dkdv_q2_kernel<D, false>), grid_kv,
+                         dim3(512), 0, s, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     const dim3 grid_q(bh, grid_blocks(bh, a.m.nq, QCfg<D>::BQ, varlen));
     hipLaunchKernelGGL(a.m.dropout ? (dq_kernel<D, true>) : (dq_kernel<D, false>), grid_q, dim3(QCfg<D>::NT),
                        0, s, a);

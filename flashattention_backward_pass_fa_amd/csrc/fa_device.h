@@ -41,12 +41,14 @@ typedef f16x8 e16x8;
 typedef f16x4 e16x4;
 #define FA_ELEM_NS_BEGIN namespace fp16 {
 #define FA_ELEM_NS_END }
+#define FA_ELEM_NS fp16::
 #else
 typedef bf16 e16;
 typedef bf16x8 e16x8;
 typedef bf16x4 e16x4;
 #define FA_ELEM_NS_BEGIN
 #define FA_ELEM_NS_END
+#define FA_ELEM_NS
 #endif
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

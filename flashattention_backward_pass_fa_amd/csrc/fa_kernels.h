@@ -48,10 +48,12 @@ struct PrepArgs {
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);  // bf16 (fp16: in namespace fp16)
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd16(const BwdArgs& a, bool deterministic, hipStream_t s);
+hipError_t launch_kv128(const BwdArgs& a, hipStream_t s);  // KV-outer, d = 128, deterministic
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
 namespace fp16 {
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd16(const BwdArgs& a, bool deterministic, hipStream_t s);
+hipError_t launch_kv128(const BwdArgs& a, hipStream_t s);
 }  // namespace fp16
 hipError_t launch_preprocess(const PrepArgs& a, hipStream_t s);
 hipError_t launch_dq_convert(const PrepArgs& a, hipStream_t s);

@@ -1,0 +1,349 @@
+// fa_kv128.hip - the KV-outer backward kernel for head dimension 128
+// (deterministic mode), 16-bit (bf16 or fp16): compiled once per element type
+// like fa_bwd16.hip, and with the instruction-level-parallelism scheduler.
+
+#include <type_traits>
+
+#include "fa_bwd_common.h"
+
+namespace fa {
+FA_ELEM_NS_BEGIN
+namespace {
+
+// --------------------------------- KV-outer, d = 128: two phases per block
+
+// P~ (the kept weights, without 1 / (1 - p)) and dS of one 32-key x 32-query
+// tile from its S = Q K^T and dP = dO V^T accumulators (keys across lanes,
+// queries inside the lane: element r of lane l is query q0 + 8 (r / 4) +
+// 4 g + r % 4, key `key`).  MASK zeroes hidden pairs; DROP applies the keep
+// mask, one Philox block per four keys shared by the lanes of a quad.
+// Returns the values as four runs of 4 consecutive queries (rr = 0..3).
+template <bool MASK, bool DROP>
+__device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const f32x16& dp,
+                                        const float* sLq, const float* sDq, int g, int b, int h,
+                                        int q0, int key, e16x4 (&pw)[4], e16x4 (&dw)[4]) {
+  uint32_t kq[4] = {0xFFFFu, 0xFFFFu, 0xFFFFu, 0xFFFFu};
+  const int t = key & 3;
+  if (DROP) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      mine |= dropout_keep4(a.m, b, h, q0 + 8 * rr + 4 * g + t, key & ~3) << (4 * rr);
+    kq[0] = __builtin_amdgcn_mov_dpp((int)mine, 0x00, 0xF, 0xF, false);  // quad_perm [0,0,0,0]
+    kq[1] = __builtin_amdgcn_mov_dpp((int)mine, 0x55, 0xF, 0xF, false);  // quad_perm [1,1,1,1]
+    kq[2] = __builtin_amdgcn_mov_dpp((int)mine, 0xAA, 0xF, 0xF, false);  // quad_perm [2,2,2,2]
+    kq[3] = __builtin_amdgcn_mov_dpp((int)mine, 0xFF, 0xF, 0xF, false);  // quad_perm [3,3,3,3]
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
+    const f32x4 d4 = *(const f32x4*)(sDq + 8 * rr + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * rr + e;
+      float p = fast_exp2(s[r] * a.scale_log2 - l4[e]);
+      if (MASK) p = visible(a.m, q0 + 8 * rr + 4 * g + e, key) ? p : 0.f;
+      float dpv = dp[r];
+      float pk = p;
+      if (DROP) {
+        const bool keep = (kq[e] >> (4 * rr + t)) & 1u;
+        pk = keep ? p : 0.f;  // 1 / (1 - p) is applied to dV at the store
+        dpv = keep ? dpv * a.m.keep_scale : 0.f;
+      }
+      pw[rr][e] = (e16)pk;
+      dw[rr][e] = (e16)(p * (dpv - d4[e]));
+    }
+  }
+}
+
+// KV-outer kernel for d = 128 with 8 waves, split into producers and
+// consumers ("FlashAttention backward", "The loop structure": dK and dV of
+// a key block accumulate in registers over the query blocks and are written
+// once).  One workgroup owns 128 keys and loops over the 64-query blocks that
+// can see them; in the iteration for block i:
+//  - producer wave p (waves 0..3) takes key group p (32 keys, K and V in
+//    registers) and all 64 queries of block i + 1: S = Q K^T and dP = dO V^T
+//    on MFMA, then P~ and dS ("Lecture 7", "The recomputation trick";
+//    "FlashAttention backward", "The gradients, and the one scalar that
+//    makes them local"), written key-major (16-bit) to one of two LDS
+//    buffers;
+//  - consumer wave c (waves 4..7) owns columns 32 c .. 32 c + 31 of dV and dK
+//    for all 128 keys and accumulates block i from the other buffer:
+//    dV += P~^T dO and dK += dS^T Q in fp32 registers.
+// Each SIMD runs one producer and one consumer, so the producers'
+// exponentials overlap the consumers' products; the consumers read each Q,
+// dO tile once (transposed, for their column slice) instead of once per key
+// group, and every dK, dV value has a single owner (no partial sums).
+template <int D>
+struct KvSCfg {
+  static constexpr int BC = 128, BR = 64, NT = 512;
+  static constexpr int LD = lds_stride(D);  // Q, dO tiles (row-major, padded)
+  // P~ and dS tiles, [key][query]: 72 elements = 36 dwords per row, an odd
+  // multiple of 4 modulo 64, so the 16-byte A-operand reads of 16 lanes
+  // (16 consecutive keys) fall on disjoint banks
+  static constexpr int LDP = BR + 8;
+  static constexpr int KT = D / 16, CH = D / 8;
+  static constexpr int LOADS = BR * CH / NT;  // Q (and dO) chunks per thread per block
+};
+
+template <int D, bool DROP>
+__device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
+  static_assert(D == 128, "four 32-column slices per matrix: one per consumer wave");
+  using C = KvSCfg<D>;
+  constexpr int TILE = C::BR * C::LD, PT = C::BC * C::LDP;
+  // [0, 4 TILE): Q, dO double buffers; then two P~ / dS buffer pairs; all of
+  // it reused for staging the output rows after the loop
+  __shared__ __attribute__((aligned(16))) e16 smem[4 * TILE + 4 * PT];
+  __shared__ __attribute__((aligned(16))) float sL[2][C::BR];
+  __shared__ __attribute__((aligned(16))) float sD[2][C::BR];
+  auto sQ = [&](int buf) { return smem + buf * TILE; };
+  auto sO = [&](int buf) { return smem + (2 + buf) * TILE; };
+  auto sP = [&](int buf) { return smem + 4 * TILE + 2 * buf * PT; };
+  auto sS = [&](int buf) { return smem + 4 * TILE + (2 * buf + 1) * PT; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, as a scalar
+  const bool producer = wu < 4;
+  const int role = wu & 3;  // producer: key group; consumer: column slice
+  const int b = bh / a.H, h = bh - b * a.H;
+  bwd_localize(a, b);
+  const int NQ = a.m.nq, NK = a.m.nk;
+  const int kv0 = blk * C::BC;
+  if (kv0 >= NK) return;  // past this sequence's keys
+  const int kvw = kv0 + 32 * role;
+  const int key = kvw + c;
+
+  // Query rows that can see at least one of the block's keys.
+  const int q_lo = max(0, kv0 - a.m.hi_off), q_hi = min(NQ, kv0 + C::BC + a.m.lo_off);
+  const int it0 = q_lo / C::BR;
+  const int it1 = q_lo < q_hi ? (q_hi + C::BR - 1) / C::BR : it0;
+
+  const int64_t row_base = (int64_t)bh * a.ln;
+  const char* q_head = (const char*)at<e16>(a.q, b, h, 0);
+  const char* o_head = (const char*)at<e16>(a.dout, b, h, 0);
+  const uint32_t q_rs = (uint32_t)a.q.sn * 2, o_rs = (uint32_t)a.dout.sn * 2;
+  e16x8 pq[C::LOADS], po[C::LOADS];
+  float pld = 0.f;
+  auto load_tile = [&](int it) {
+    const int q0 = it * C::BR;
+#pragma unroll
+    for (int x = 0; x < C::LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      const int qr = min(q0 + row, NQ - 1);  // rows past the end are masked: read a valid one
+      pq[x] = load8((const e16*)row_addr(q_head, q_rs, qr) + col);
+      po[x] = load8((const e16*)row_addr(o_head, o_rs, qr) + col);
+    }
+    if (tid < 2 * C::BR)
+      pld = (tid < C::BR ? a.lse : a.delta)[row_base + min(q0 + (tid & (C::BR - 1)), NQ - 1)];
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < C::LOADS; ++x) {
+      const int chunk = tid + x * C::NT;
+      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
+      store8(sQ(buf) + row * C::LD + col, pq[x]);
+      store8(sO(buf) + row * C::LD + col, po[x]);
+    }
+    if (tid < C::BR) sL[buf][tid] = pld * kLog2e;
+    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = pld;
+  };
+
+  // Query blocks [itA, itB) see all 128 keys with no mask edge: the first
+  // query must reach the last key, the last query must still see the first.
+  int itA = it1, itB = it1;
+  if (kv0 + C::BC <= NK) {
+    const int lo = max(0, kv0 + C::BC - 1 - a.m.hi_off);
+    const int hi = min(NQ - C::BR, kv0 - C::BR + 1 + a.m.lo_off);
+    if (lo <= hi) {
+      itA = min(max(it0, (lo + C::BR - 1) / C::BR), it1);
+      itB = max(itA, min(it1, hi / C::BR + 1));
+    }
+  }
+  auto is_full = [&](int it) { return it >= itA && it < itB; };
+  std::integral_constant<bool, false> general;
+  std::integral_constant<bool, true> fast;
+
+  // The two roles run separate copies of the loop (so that neither holds the
+  // other's registers) with the same barriers in the same order.  Iteration
+  // it: consumers take block it (tile and P~/dS buffer (it - it0) & 1),
+  // producers block it + 1 (the other ones); then every thread stores block
+  // it + 2's Q, dO (loaded during the iteration) into the tile block it used.
+  // The first iteration is preceded by block it0's Q, dO and P~, dS, and
+  // block it0 + 1's Q, dO.
+  if (producer) {
+    if (it0 < it1) load_tile(it0);
+    // K and V rows: B operands of S and dP, in registers for the whole loop
+    e16x8 kreg[C::KT], vreg[C::KT];
+    {
+      const e16* kp = at<e16>(a.k, b, h, min(key, NK - 1));
+      const e16* vp = at<e16>(a.v, b, h, min(key, NK - 1));
+#pragma unroll
+      for (int t = 0; t < C::KT; ++t) {
+        kreg[t] = load8(kp + 16 * t + 8 * g);
+        vreg[t] = load8(vp + 16 * t + 8 * g);
+      }
+    }
+    if (it0 < it1) store_tile(0);
+    // K and V must have landed before the loop: the wait counter cannot tell
+    // them from later prefetches, so a register still pending here would
+    // make every iteration wait for its own prefetch.
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    lds_barrier();
+    // P~ and dS of block it (both 32-query halves) into buffer pb
+    auto produce = [&](int it, int qb, int pb, auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      const e16* Qs = sQ(qb);
+      const e16* Os = sO(qb);
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        const int qs = it * C::BR + 32 * qh;
+        e16* prow = sP(pb) + (32 * role + c) * C::LDP + 32 * qh + 4 * g;
+        e16* srow = sS(pb) + (32 * role + c) * C::LDP + 32 * qh + 4 * g;
+        if (!FULL && block_dead(a.m, qs, 32, kvw, 32)) {
+          // a fully hidden tile contributes zeros (the consumers run every
+          // tile's products, without branches)
+          const e16x4 z4 = {(e16)0.f, (e16)0.f, (e16)0.f, (e16)0.f};
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            *(e16x4*)(prow + 8 * rr) = z4;
+            *(e16x4*)(srow + 8 * rr) = z4;
+          }
+          continue;
+        }
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        const e16* qrow = Qs + (32 * qh + c) * C::LD + 8 * g;
+        const e16* orow = Os + (32 * qh + c) * C::LD + 8 * g;
+#pragma unroll
+        for (int t = 0; t < C::KT; ++t) sacc = mfma32x32x16(load8(qrow + 16 * t), kreg[t], sacc);
+#pragma unroll
+        for (int t = 0; t < C::KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), vreg[t], dpacc);
+        e16x4 pw[4], dw[4];
+        const float* sLq = &sL[qb][32 * qh];
+        const float* sDq = &sD[qb][32 * qh];
+        if (FULL) kv_p_ds<false, DROP>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pw, dw);
+        else kv_p_ds<true, DROP>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pw, dw);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          *(e16x4*)(prow + 8 * rr) = pw[rr];
+          *(e16x4*)(srow + 8 * rr) = dw[rr];
+        }
+      }
+    };
+    if (it0 < it1) {
+      if (it0 + 1 < it1) load_tile(it0 + 1);
+      if (is_full(it0)) produce(it0, 0, 0, fast);
+      else produce(it0, 0, 0, general);
+      if (it0 + 1 < it1) store_tile(1);
+      lds_barrier();
+    }
+    for (int it = it0; it < it1; ++it) {
+      const int cur = (it - it0) & 1, nxt = cur ^ 1;
+      const bool has_next2 = it + 2 < it1;
+      if (has_next2) load_tile(it + 2);
+      if (it + 1 < it1) {
+        if (is_full(it + 1)) produce(it + 1, nxt, nxt, fast);
+        else produce(it + 1, nxt, nxt, general);
+      }
+      lds_barrier();
+      if (has_next2) {
+        store_tile(cur);
+        lds_barrier();
+      }
+    }
+  } else {
+    const int n0 = 32 * role;  // this consumer's columns of dV and dK
+    f32x16 acc_v[4], acc_k[4];  // one 32-key tile per key group
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc_v[m] = f32x16{};
+      acc_k[m] = f32x16{};
+    }
+    if (it0 < it1) {
+      load_tile(it0);
+      store_tile(0);
+    }
+    lds_barrier();
+    // acc += A^T B over block it's queries, A = P~ (dV) or dS (dK) read
+    // key-major from buffer pb, B = dO or Q read transposed from tile qb
+    auto consume = [&](int qb, int pb) {
+      const e16* Pt = sP(pb);
+      const e16* St = sS(pb);
+#pragma unroll
+      for (int ks = 0; ks < C::BR / 16; ++ks) {  // 16-query k-steps
+        const e16x8 bo = tr_operand(sO(qb), C::LD, 16 * ks + 8 * g, 16 * ks + 8 * g + 4, n0, lane);
+        const e16x8 bq = tr_operand(sQ(qb), C::LD, 16 * ks + 8 * g, 16 * ks + 8 * g + 4, n0, lane);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int off = (32 * m + c) * C::LDP + 16 * ks + 8 * g;
+          acc_v[m] = mfma32x32x16(load8(Pt + off), bo, acc_v[m]);
+          acc_k[m] = mfma32x32x16(load8(St + off), bq, acc_k[m]);
+        }
+      }
+    };
+    if (it0 < it1) {
+      if (it0 + 1 < it1) {
+        load_tile(it0 + 1);
+        store_tile(1);
+      }
+      lds_barrier();
+    }
+    for (int it = it0; it < it1; ++it) {
+      const int cur = (it - it0) & 1;
+      const bool has_next2 = it + 2 < it1;
+      if (has_next2) load_tile(it + 2);
+      consume(cur, cur);
+      lds_barrier();
+      if (has_next2) {
+        store_tile(cur);
+        lds_barrier();
+      }
+    }
+    // dK = sm_scale dS^T Q and dV = (Z o P)^T dO / (1 - p), rounded once to
+    // the element type: each consumer writes its slices row-major into LDS
+    // (free after the loop's last barrier); after the barrier below every
+    // thread stores whole 8-column chunks with 16-byte stores.
+    constexpr int SR = D + 8;
+    static_assert(2 * C::BC * SR <= 4 * TILE + 4 * PT, "both outputs must fit the LDS staging");
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
+        smem[row * SR + n0 + c] = (e16)(acc_v[m][r] * a.m.keep_scale);
+        smem[(C::BC + row) * SR + n0 + c] = (e16)(acc_k[m][r] * a.sm_scale);
+      }
+  }
+
+  constexpr int SR = D + 8, CPR = D / 8;
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2 * C::BC * CPR / C::NT; ++x) {
+    const int chunk = tid + x * C::NT;
+    const int row = chunk / CPR, col = (chunk % CPR) * 8;  // rows [0, BC): dV, [BC, 2 BC): dK
+    const int kr = kv0 + (row & (C::BC - 1));
+    if (kr < NK)
+      store8(at<e16>(row < C::BC ? a.dv : a.dk, b, h, kr) + col, *(const e16x8*)(smem + row * SR + col));
+  }
+}
+
+template <int D, bool DROP>
+__global__ void __launch_bounds__(512) dkdv_ws_kernel(BwdArgs a) {
+  int bh, blk;
+  wg_coords(a.m.cu_q != nullptr, bh, blk);
+  dkdv_ws_body<D, DROP>(a, bh, blk);
+}
+
+}  // namespace
+
+hipError_t launch_kv128(const BwdArgs& a, hipStream_t s) {
+  const int bh = a.B * a.H;
+  const dim3 grid(bh, grid_blocks(bh, a.m.nk, KvSCfg<128>::BC, a.m.cu_q != nullptr));
+  hipLaunchKernelGGL(a.m.dropout ? (dkdv_ws_kernel<128, true>) : (dkdv_ws_kernel<128, false>), grid,
+                     dim3(KvSCfg<128>::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+FA_ELEM_NS_END
+}  // namespace fa
