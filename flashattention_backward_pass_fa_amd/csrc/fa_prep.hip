@@ -1,7 +1,7 @@
 // fa_prep.hip - HBM-bound helper kernels of the backward.
 //
-//  prep_kernel        D_i = sum_k dO_ik O_ik for every row, fp32 accumulate
-//                     ("FlashAttention backward", section "The gradients, and
+//  prep16_kernel,     D_i = sum_k dO_ik O_ik for every row, fp32 accumulate
+//  prep_f32_kernel    ("FlashAttention backward", section "The gradients, and
 //                     the one scalar that makes them local": a single
 //                     streaming pass over O and dO ahead of the backward
 //                     kernels), fused with zeroing the fp32 dQ accumulator of
@@ -9,33 +9,18 @@
 //  dq_convert_kernel  dQ = round_to_dtype(sm_scale * dQ_acc) (bf16 or fp16).
 //  mask_kernel        the dropout keep mask of one head (test aid).
 //
-// prep_kernel: 16 lanes per row, each lane loads 16 contiguous bytes of O
-// and dO per step (fully coalesced rows), multiplies in fp32, and the 16
-// partial sums are combined with lane shuffles.  Rows are walked
-// grid-stride so the grid can be sized to the machine.
+// prep16_kernel (bf16/fp16, d = 64 or 128): d / 8 lanes per row, each lane
+// one 16-byte chunk of O and of dO per row (fully coalesced rows), two rows
+// per thread at d = 128 and four at d = 64 with every load issued before the
+// first use; fp32 products, lane-shuffle reduction.  prep_f32_kernel covers fp32 and other d.  Rows
+// are walked grid-stride so the grid can be sized to the machine.
 
 #include "fa_kernels.h"
 
 namespace fa {
 namespace {
 
-constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per row
-
-// this lane's share of sum_k dO_k O_k over a 16-bit row (8 elements per step)
-template <typename T, typename T8>
-__device__ __forceinline__ float row_dot16(const TensorView& o, const TensorView& g, int b, int h, int n,
-                                           int d, int sub) {
-  const T* op = at<T>(o, b, h, n);
-  const T* gp = at<T>(g, b, h, n);
-  float acc = 0.f;
-  for (int c0 = sub * 8; c0 < d; c0 += 128) {
-    const T8 ov = *(const T8*)(op + c0);
-    const T8 gv = *(const T8*)(gp + c0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)ov[e], (float)gv[e], acc);
-  }
-  return acc;
-}
+constexpr int kRowsPerBlock = 16;  // fp32 path: 256 threads, 16 lanes per row
 
 template <typename T, typename T8>
 __device__ __forceinline__ void store_scaled8(T* dst, f32x4 x0, f32x4 x1, float scale) {
@@ -59,37 +44,97 @@ __device__ __forceinline__ void zero_acc_row(const PrepArgs& a, int64_t row, int
   }
 }
 
-__global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
+// Packed row (b, h, n) of flat index `row`: its batch, head and sequence
+// position (varlen: rows past sequence b's length hold no query, n < 0).
+__device__ __forceinline__ void row_coords(const PrepArgs& a, int64_t row, int& b, int& h, int& n) {
+  const int64_t HN = (int64_t)a.H * a.N;
+  if (row < (int64_t)INT32_MAX && HN < (int64_t)INT32_MAX) {  // 32-bit division: a 64-bit one is a long software sequence
+    const uint32_t r32 = (uint32_t)row, hn = (uint32_t)HN;
+    b = (int)(r32 / hn);
+    const uint32_t rem = r32 - (uint32_t)b * hn;
+    h = (int)(rem / (uint32_t)a.N);
+    n = (int)(rem - (uint32_t)h * (uint32_t)a.N);
+  } else {
+    b = (int)(row / HN);
+    const int rem = (int)(row - b * HN);
+    h = rem / a.N;
+    n = rem - h * a.N;
+  }
+  if (a.cu_q) {
+    const int q0 = a.cu_q[b];
+    n = n < a.cu_q[b + 1] - q0 ? n + q0 : -1;
+  }
+}
+
+// 16-bit rows: D / 8 lanes per row, each lane one 16-byte chunk of O and of
+// dO per row, and R rows per thread whose loads are all issued before the
+// first is used (more bytes in flight per thread: the pass is bound by HBM
+// latency, not arithmetic).  The partial sums of a row's lanes are combined
+// with lane shuffles.
+template <typename T, typename T8, int D, int R, bool STREAM>
+__global__ void __launch_bounds__(256) prep16_kernel(PrepArgs a) {
+  constexpr int LPR = D / 8, SLOTS = 256 / LPR;  // lanes per row, rows per block pass
+  const int sub = threadIdx.x % LPR, slot = threadIdx.x / LPR;
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  for (int64_t base = (int64_t)blockIdx.x * SLOTS * R; base < rows; base += (int64_t)gridDim.x * SLOTS * R) {
+    T8 ov[R], gv[R];
+    int64_t rr[R];
+    bool ok[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      rr[k] = base + slot + (int64_t)k * SLOTS;
+      int b = 0, h = 0, n = -1;
+      if (rr[k] < rows) row_coords(a, rr[k], b, h, n);
+      ok[k] = n >= 0;
+      // rows without a query read a valid row (their result is dropped):
+      // an unconditional load does not make the thread wait for it here
+      const T* op = at<T>(a.o, b, h, ok[k] ? n : 0);
+      const T* gp = at<T>(a.dout, b, h, ok[k] ? n : 0);
+      if (STREAM) {  // read once: no reason to keep the lines in cache
+        ov[k] = __builtin_nontemporal_load((const T8*)(op + 8 * sub));
+        gv[k] = __builtin_nontemporal_load((const T8*)(gp + 8 * sub));
+      } else {
+        ov[k] = *(const T8*)(op + 8 * sub);
+        gv[k] = *(const T8*)(gp + 8 * sub);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (rr[k] >= rows) continue;
+      float acc = 0.f;
+      if (ok[k]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)ov[k][e], (float)gv[k][e], acc);
+      }
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+      if (ok[k] && sub == 0) a.delta[rr[k]] = acc;
+      if (a.dq_acc) {  // atomic mode: this row of the fp32 dQ accumulator starts at zero
+        f32x4* z = (f32x4*)(a.dq_acc + rr[k] * D) + 2 * sub;
+        z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+}
+
+// fp32 rows (any d): 16 lanes per row, grid-stride over rows.
+__global__ void __launch_bounds__(256) prep_f32_kernel(PrepArgs a) {
   const int sub = threadIdx.x & 15;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  const int64_t HN = (int64_t)a.H * a.N;
   for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < rows;
        row += (int64_t)gridDim.x * kRowsPerBlock) {
-    const int b = (int)(row / HN);
-    const int rem = (int)(row - b * HN);
-    const int h = rem / a.N;
-    int n = rem - h * a.N;
-    if (a.cu_q) {  // varlen: rows past sequence b's length hold no query
-      const int q0 = a.cu_q[b];
-      if (n >= a.cu_q[b + 1] - q0) {
-        zero_acc_row(a, row, sub);
-        continue;
-      }
-      n += q0;
-    }
+    int b, h, n;
+    row_coords(a, row, b, h, n);
     float acc = 0.f;
-    if (a.dtype == 1) {
-      acc = row_dot16<bf16, bf16x8>(a.o, a.dout, b, h, n, a.d, sub);
-    } else if (a.dtype == 2) {
-      acc = row_dot16<f16, f16x8>(a.o, a.dout, b, h, n, a.d, sub);
-    } else {
+    if (n >= 0) {
       const float* op = at<float>(a.o, b, h, n);
       const float* gp = at<float>(a.dout, b, h, n);
       for (int c = sub; c < a.d; c += 16) acc = fmaf(op[c], gp[c], acc);
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (sub == 0) a.delta[row] = acc;
+    if (n >= 0 && sub == 0) a.delta[row] = acc;
     zero_acc_row(a, row, sub);
   }
 }
@@ -139,7 +184,23 @@ int grid_for(int64_t work_items, int per_block) {
 
 hipError_t launch_preprocess(const PrepArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  hipLaunchKernelGGL(prep_kernel, dim3(grid_for(rows, kRowsPerBlock)), dim3(256), 0, s, a);
+  if (a.dtype == 0 || (a.d != 64 && a.d != 128)) {
+    hipLaunchKernelGGL(prep_f32_kernel, dim3(grid_for(rows, kRowsPerBlock)), dim3(256), 0, s, a);
+  } else if (a.d == 128) {
+    // 2 rows per thread (16 rows per block pass); measured best of 1, 2, 4, 8
+    const dim3 grid(grid_for(rows, 16 * 2));
+    if (a.dtype == 1)
+      hipLaunchKernelGGL((prep16_kernel<bf16, bf16x8, 128, 2, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prep16_kernel<f16, f16x8, 128, 2, false>), grid, dim3(256), 0, s, a);
+  } else {
+    // 4 rows per thread (32 rows per block pass), non-temporal loads
+    const dim3 grid(grid_for(rows, 32 * 4));
+    if (a.dtype == 1)
+      hipLaunchKernelGGL((prep16_kernel<bf16, bf16x8, 64, 4, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prep16_kernel<f16, f16x8, 64, 4, true>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
