@@ -17,7 +17,8 @@ namespace {
 // queries inside the lane: element r of lane l is query q0 + 8 (r / 4) +
 // 4 g + r % 4, key `key`).  MASK zeroes hidden pairs; DROP applies the keep
 // mask, one Philox block per four keys shared by the lanes of a quad.
-// Returns the values as four runs of 4 consecutive queries (rr = 0..3).
+// sDq holds -D.  Returns the values as four runs of 4 consecutive queries
+// (rr = 0..3).
 template <bool MASK, bool DROP>
 __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const f32x16& dp,
                                         const float* sLq, const float* sDq, int g, int b, int h,
@@ -37,7 +38,7 @@ __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
-    const f32x4 d4 = *(const f32x4*)(sDq + 8 * rr + 4 * g);
+    const f32x4 nd4 = *(const f32x4*)(sDq + 8 * rr + 4 * g);  // -D
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
@@ -51,7 +52,7 @@ __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const
         dpv = keep ? dpv * a.m.keep_scale : 0.f;
       }
       pw[rr][e] = (e16)pk;
-      dw[rr][e] = (e16)(p * (dpv - d4[e]));
+      dw[rr][e] = (e16)(p * (dpv + nd4[e]));
     }
   }
 }
@@ -147,7 +148,7 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
       store8(sO(buf) + row * C::LD + col, po[x]);
     }
     if (tid < C::BR) sL[buf][tid] = pld * kLog2e;
-    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = pld;
+    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = -pld;  // -D: the start value of dP - D
   };
 
   // Query blocks [itA, itB) see all 128 keys with no mask edge: the first
@@ -231,10 +232,93 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
         }
       }
     };
+    // A block with no mask edge, without dropout, scheduled by hand: the 16
+    // products of the second 32-query half are issued among the first
+    // half's elementwise work, so that this wave's exponentials run beside
+    // its own matrix products instead of after them.  Operands are read
+    // AHEAD products early, and dP accumulates from -D, so the product ends
+    // as dP - D.  Each step (two products) is fenced so the compiler keeps
+    // this order.
+    auto produce_full = [&](int it, int qb, int pb) {
+      constexpr int AHEAD = 4;
+      const e16* qa = sQ(qb) + c * C::LD + 8 * g;
+      const e16* oa = sO(qb) + c * C::LD + 8 * g;
+      // product j: query half j / 16, S = Q K^T (j % 16 < 8) or dP = dO V^T,
+      // k-step j % 8
+      auto operand = [&](int j) {
+        return load8(((j & 15) < 8 ? qa : oa) + (j >> 4) * 32 * C::LD + 16 * (j & 7));
+      };
+      auto minus_d = [&](int half) {
+        f32x16 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 d4 = *(const f32x4*)&sD[qb][32 * half + 8 * rr + 4 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * rr + e] = d4[e];
+        }
+        return v;
+      };
+      auto log2_l = [&](int half, f32x4 (&l)[4]) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) l[rr] = *(const f32x4*)&sL[qb][32 * half + 8 * rr + 4 * g];
+      };
+      e16* prow = sP(pb) + (32 * role + c) * C::LDP + 4 * g;
+      e16* srow = sS(pb) + (32 * role + c) * C::LDP + 4 * g;
+      f32x16 acc[4];  // S, dP - D of half 0, then of half 1
+      f32x4 lq[2][4];
+      e16x4 pw, dw;
+      // P~ = exp2(S scale_log2 - L log2 e) and dS = P~ (dP - D) for
+      // elements e, e + 1 of a half; a run of 4 queries is stored when done
+      auto pair = [&](int half, int e) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = e + u;
+          const float p = fast_exp2(acc[2 * half][r] * a.scale_log2 - lq[half][r >> 2][r & 3]);
+          pw[r & 3] = (e16)p;
+          dw[r & 3] = (e16)(p * acc[2 * half + 1][r]);
+        }
+        if ((e & 3) == 2) {
+          *(e16x4*)(prow + 32 * half + 8 * (e >> 2)) = pw;
+          *(e16x4*)(srow + 32 * half + 8 * (e >> 2)) = dw;
+        }
+      };
+      e16x8 op[AHEAD];
+#pragma unroll
+      for (int j = 0; j < AHEAD; ++j) op[j] = operand(j);
+      acc[0] = f32x16{};
+      acc[1] = minus_d(0);
+      acc[2] = f32x16{};
+      log2_l(0, lq[0]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int jj = j + u;
+          acc[jj >> 3] = mfma32x32x16(op[jj % AHEAD], (jj & 15) < 8 ? kreg[jj & 7] : vreg[jj & 7], acc[jj >> 3]);
+          if (jj + AHEAD < 32) op[jj % AHEAD] = operand(jj + AHEAD);
+        }
+        if (j == 8) {
+          acc[3] = minus_d(1);
+          log2_l(1, lq[1]);
+        }
+        if (j >= 16) pair(0, j - 16);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) pair(1, e);
+    };
+    auto produce_any = [&](int it, int qb, int pb) {
+      if (is_full(it)) {
+        if constexpr (DROP) produce(it, qb, pb, fast);
+        else produce_full(it, qb, pb);
+      } else {
+        produce(it, qb, pb, general);
+      }
+    };
     if (it0 < it1) {
       if (it0 + 1 < it1) load_tile(it0 + 1);
-      if (is_full(it0)) produce(it0, 0, 0, fast);
-      else produce(it0, 0, 0, general);
+      produce_any(it0, 0, 0);
       if (it0 + 1 < it1) store_tile(1);
       lds_barrier();
     }
@@ -242,10 +326,7 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
       const int cur = (it - it0) & 1, nxt = cur ^ 1;
       const bool has_next2 = it + 2 < it1;
       if (has_next2) load_tile(it + 2);
-      if (it + 1 < it1) {
-        if (is_full(it + 1)) produce(it + 1, nxt, nxt, fast);
-        else produce(it + 1, nxt, nxt, general);
-      }
+      if (it + 1 < it1) produce_any(it + 1, nxt, nxt);
       lds_barrier();
       if (has_next2) {
         store_tile(cur);
