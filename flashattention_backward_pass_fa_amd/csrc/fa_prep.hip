@@ -71,7 +71,7 @@ __device__ __forceinline__ void row_coords(const PrepArgs& a, int64_t row, int& 
 // first is used (more bytes in flight per thread: the pass is bound by HBM
 // latency, not arithmetic).  The partial sums of a row's lanes are combined
 // with lane shuffles.
-template <typename T, typename T8, int D, int R, bool STREAM>
+template <typename T, typename T8, int D, int R, bool STREAM, bool CONTIG>
 __global__ void __launch_bounds__(256) prep16_kernel(PrepArgs a) {
   constexpr int LPR = D / 8, SLOTS = 256 / LPR;  // lanes per row, rows per block pass
   const int sub = threadIdx.x % LPR, slot = threadIdx.x / LPR;
@@ -83,13 +83,21 @@ __global__ void __launch_bounds__(256) prep16_kernel(PrepArgs a) {
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       rr[k] = base + slot + (int64_t)k * SLOTS;
-      int b = 0, h = 0, n = -1;
-      if (rr[k] < rows) row_coords(a, rr[k], b, h, n);
-      ok[k] = n >= 0;
-      // rows without a query read a valid row (their result is dropped):
-      // an unconditional load does not make the thread wait for it here
-      const T* op = at<T>(a.o, b, h, ok[k] ? n : 0);
-      const T* gp = at<T>(a.dout, b, h, ok[k] ? n : 0);
+      const T* op;
+      const T* gp;
+      if (CONTIG) {  // [B, H, N, d] without gaps: row r starts at r * d
+        ok[k] = rr[k] < rows;
+        op = (const T*)a.o.ptr + (ok[k] ? rr[k] : 0) * D;
+        gp = (const T*)a.dout.ptr + (ok[k] ? rr[k] : 0) * D;
+      } else {
+        int b = 0, h = 0, n = -1;
+        if (rr[k] < rows) row_coords(a, rr[k], b, h, n);
+        ok[k] = n >= 0;
+        // rows without a query read a valid row (their result is dropped):
+        // an unconditional load does not make the thread wait for it here
+        op = at<T>(a.o, b, h, ok[k] ? n : 0);
+        gp = at<T>(a.dout, b, h, ok[k] ? n : 0);
+      }
       if (STREAM) {  // read once: no reason to keep the lines in cache
         ov[k] = __builtin_nontemporal_load((const T8*)(op + 8 * sub));
         gv[k] = __builtin_nontemporal_load((const T8*)(gp + 8 * sub));
@@ -180,26 +188,36 @@ int grid_for(int64_t work_items, int per_block) {
   return (int)blocks;
 }
 
+// Are a view's rows packed back to back in [B, H, N, d] order?
+bool packed_rows(const TensorView& t, const PrepArgs& a) {
+  return t.sn == a.d && t.sh == (int64_t)a.N * a.d && (a.B == 1 || t.sb == (int64_t)a.H * a.N * a.d);
+}
+
 }  // namespace
 
 hipError_t launch_preprocess(const PrepArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const bool contig = !a.cu_q && packed_rows(a.o, a) && packed_rows(a.dout, a);
   if (a.dtype == 0 || (a.d != 64 && a.d != 128)) {
     hipLaunchKernelGGL(prep_f32_kernel, dim3(grid_for(rows, kRowsPerBlock)), dim3(256), 0, s, a);
   } else if (a.d == 128) {
     // 2 rows per thread (16 rows per block pass); measured best of 1, 2, 4, 8
     const dim3 grid(grid_for(rows, 16 * 2));
     if (a.dtype == 1)
-      hipLaunchKernelGGL((prep16_kernel<bf16, bf16x8, 128, 2, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(contig ? (prep16_kernel<bf16, bf16x8, 128, 2, false, true>)
+                                : (prep16_kernel<bf16, bf16x8, 128, 2, false, false>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((prep16_kernel<f16, f16x8, 128, 2, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(contig ? (prep16_kernel<f16, f16x8, 128, 2, false, true>)
+                                : (prep16_kernel<f16, f16x8, 128, 2, false, false>), grid, dim3(256), 0, s, a);
   } else {
     // 4 rows per thread (32 rows per block pass), non-temporal loads
     const dim3 grid(grid_for(rows, 32 * 4));
     if (a.dtype == 1)
-      hipLaunchKernelGGL((prep16_kernel<bf16, bf16x8, 64, 4, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(contig ? (prep16_kernel<bf16, bf16x8, 64, 4, true, true>)
+                                : (prep16_kernel<bf16, bf16x8, 64, 4, true, false>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((prep16_kernel<f16, f16x8, 64, 4, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(contig ? (prep16_kernel<f16, f16x8, 64, 4, true, true>)
+                                : (prep16_kernel<f16, f16x8, 64, 4, true, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
