@@ -863,7 +863,10 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
     lds_barrier();
     ++jt;
   };
-  if (jtA < jtB) fast_range(std::integral_constant<bool, DROP>());
+  // With dropout at d = 128 the pipelined range's second set of S^T, dP^T
+  // accumulators and the Philox state do not fit beside the rest without
+  // spilling: every block then takes the per-block sequence.
+  if (jtA < jtB && !(DROP && D == 128)) fast_range(std::integral_constant<bool, DROP>());
   for (; jt < jt1; ++jt) general(jt);
 
   // dQ = sm_scale dS K: the waves write their rows (rounded) row-major into
