@@ -14,7 +14,7 @@ TFLOP/s (10 d FLOPs per visible pair), the roofline of the dominant launch
 dense MFMA peak, and the CPU oracle timed on one head of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode atomic|deterministic]
-                       [--workload NAME] [--no-cpu-baseline] [--side-checks]
+                       [--workload NAME] [--dropout-p P] [--no-cpu-baseline] [--side-checks]
 """
 
 import argparse
@@ -32,7 +32,10 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 (= fp16) FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_bwd16.hip",
+KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_kv128.hip",
+                  "flashattention_backward_pass_fa_amd/csrc/fa_bwd16.hip",
+                  "flashattention_backward_pass_fa_amd/csrc/fa_bwd_common.h",
+                  "flashattention_backward_pass_fa_amd/csrc/fa_prep.hip",
                   "flashattention_backward_pass_fa_amd/csrc/fa_device.h"]
 TRAFFIC_FILE = "profiles/fa_bwd_{mode}_train_causal_bf16_traffic.md"
 KERNELS_FILE = "profiles/fa_bwd_train_causal_bf16_kernels.md"
@@ -79,7 +82,7 @@ def profiled_kernel_ms(mode):
     text = _profile_text(KERNELS_FILE)
     if text is None:
         return None
-    names = (["dkdv_q2_kernel<128, false>", "dq_kernel<128, false>"] if mode == "deterministic"
+    names = (["dkdv_ws_kernel<128, false>", "dq_kernel<128, false>"] if mode == "deterministic"
              else ["dkdv_atomic_kernel<128>", "dq_convert_kernel"])
     out = {}
     for line in text.splitlines():
@@ -157,6 +160,9 @@ def main():
     ap.add_argument("--mode", choices=["atomic", "deterministic"], default="deterministic")
     ap.add_argument("--workload", default="train_causal_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout-p", type=float, default=None,
+                    help="override the workload's dropout probability (counter runs compare "
+                         "the same shape with and without the keep mask)")
     ap.add_argument("--side-checks", action="store_true",
                     help="also time fa_fwd, the non-causal backward at the same shape and the "
                          "same tokens packed as variable-length sequences (kept out of the "
@@ -177,6 +183,9 @@ def main():
     from flashattention_backward_pass_fa_amd.inputs import WORKLOADS, make_workload_inputs
 
     w = WORKLOADS[args.workload]
+    if args.dropout_p is not None:
+        import dataclasses
+        w = dataclasses.replace(w, dropout_p=args.dropout_p)
     if w.dtype not in ("bf16", "f16"):
         print("bench.py measures the 16-bit (bf16, fp16) workloads", file=sys.stderr)
         sys.exit(2)
@@ -320,8 +329,9 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     achieved = flops / (bwd_avg * 1e-3) / 1e12
-    # the committed counter summary covers the default workload only
-    traffic = measured_traffic(args.mode) if w.name == "train_causal_bf16" else None
+    # the committed profile summaries cover the default workload only
+    profiled = w.name == "train_causal_bf16" and args.dropout_p is None
+    traffic = measured_traffic(args.mode) if profiled else None
     pre_avg = sum(pre_ms) / len(pre_ms)
     pre_bytes = 2 * w.B * w.H * w.N * w.d * 2 + 4 * w.B * w.H * w.N + ws_bytes
 
@@ -366,7 +376,7 @@ def main():
     # runs lower.  The device's reported peak clock, the clock the committed
     # counter run measured on these kernels, and the peak at that clock.
     max_mhz = device_max_clock_mhz(torch)
-    load_mhz = profiled_clock_mhz() if w.name == "train_causal_bf16" else None
+    load_mhz = profiled_clock_mhz() if profiled else None
     line["clock"] = {"device_max_mhz": max_mhz, "under_load_mhz": load_mhz,
                      "source": CLOCK_FILE if load_mhz else None}
     if load_mhz:
@@ -374,7 +384,7 @@ def main():
         line["roofline_at_clock"] = {"peak": round(peak_clk, 1), "achieved": round(achieved, 2),
                                      "frac": round(achieved / peak_clk, 4),
                                      "value_frac": round(tflops / peak_clk, 4)}
-    split = profiled_kernel_ms(args.mode) if w.name == "train_causal_bf16" else None
+    split = profiled_kernel_ms(args.mode) if profiled else None
     if split:
         line["kernels_ms_profiled"] = dict(split, source=KERNELS_FILE)
     fwd_flops = flops * 4 / 10  # forward: S and O products, 4 d per visible pair
