@@ -733,10 +733,19 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
 #pragma unroll
   for (int n = 0; n < C::DT; ++n) dq_acc[n] = f32x16{};
 
+  // dP^T accumulates from -D, so that without dropout the product ends as
+  // dP - D; with dropout from -D (1 - p), so that a kept element's
+  // dP / (1 - p) - D is one multiply (a dropped one is -D)
+  f32x16 dp0;
+  {
+    const float start = DROP ? -dd / a.m.keep_scale : -dd;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp0[r] = start;
+  }
   // S^T, dP^T of one 32-key block against this wave's queries
   auto sdp = [&](int buf, f32x16& st, f32x16& dpt) {
     st = f32x16{};
-    dpt = f32x16{};
+    dpt = dp0;
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) {
       st = mfma32x32x16(load8(&sK[buf][c * C::LD + 16 * t + 8 * g]), qreg[t], st);
@@ -803,10 +812,10 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
           float p = fast_exp2(st[r] * a.scale_log2 - l2);
-          float dpv = dpt[r];
+          float dmd = dpt[r];  // dP - D (dropout: with dP scaled by 1 - p)
           p = visible(a.m, myq, j4 + e) ? p : 0.f;
-          if (DROP) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
-          const e16 v = (e16)(p * (dpv - dd));
+          if (DROP) dmd = (keep >> e) & 1u ? dmd * a.m.keep_scale : -dd;
+          const e16 v = (e16)(p * dmd);
           if (r < 8) d0[r] = v; else d1[r - 8] = v;
         }
       }
@@ -827,9 +836,9 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
-          float dpv = dpt[r];
-          if (FDROP) dpv = (keep >> e) & 1u ? dpv * a.m.keep_scale : 0.f;
-          const e16 v = (e16)(fast_exp2(st[r] * a.scale_log2 - l2) * (dpv - dd));
+          float dmd = dpt[r];
+          if (FDROP) dmd = (keep >> e) & 1u ? dmd * a.m.keep_scale : -dd;
+          const e16 v = (e16)(fast_exp2(st[r] * a.scale_log2 - l2) * dmd);
           if (r < 8) d0[r] = v; else d1[r - 8] = v;
         }
       }
