@@ -36,7 +36,8 @@ KERNEL_SOURCES = ["flashattention_backward_pass_fa_amd/csrc/fa_kv128.hip",
                   "flashattention_backward_pass_fa_amd/csrc/fa_bwd16.hip",
                   "flashattention_backward_pass_fa_amd/csrc/fa_bwd_common.h",
                   "flashattention_backward_pass_fa_amd/csrc/fa_prep.hip",
-                  "flashattention_backward_pass_fa_amd/csrc/fa_device.h"]
+                  "flashattention_backward_pass_fa_amd/csrc/fa_device.h",
+                  "flashattention_backward_pass_fa_amd/build.py"]
 TRAFFIC_FILE = "profiles/fa_bwd_{mode}_train_causal_bf16_traffic.md"
 KERNELS_FILE = "profiles/fa_bwd_train_causal_bf16_kernels.md"
 CLOCK_FILE = "profiles/fa_bwd_train_causal_bf16_clock.md"
