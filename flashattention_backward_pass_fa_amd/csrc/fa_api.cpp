@@ -50,7 +50,7 @@ fa_status check_params(const fa_params* p) {
   if (p->window_left < -1 || p->window_right < -1) return FA_ERR_INVALID_VALUE;
   if (!(p->dropout_p >= 0.0 && p->dropout_p < 1.0)) return FA_ERR_INVALID_VALUE;
   if (p->dropout_p > 0.0) {
-    if (std::ceil(p->dropout_p * 4294967296.0) > 4294967295.0) return FA_ERR_INVALID_VALUE;
+    if (std::ceil(p->dropout_p * 65536.0) > 65535.0) return FA_ERR_INVALID_VALUE;
     if (p->batch > 65536 || p->heads > 65536 || p->seqlen > 65536 || p->seqlen_k > 65536)
       return FA_ERR_NOT_SUPPORTED;
   }
@@ -125,7 +125,7 @@ fa::MaskArgs mask_args(const fa_params* p) {
   m.cu_q = p->cu_seqlens_q;
   m.cu_k = p->cu_seqlens_k;
   m.dropout = p->dropout_p > 0.0 ? 1 : 0;
-  m.keep_threshold = (uint32_t)std::ceil(p->dropout_p * 4294967296.0);
+  m.keep_threshold = (uint32_t)std::ceil(p->dropout_p * 65536.0);  // of a 16-bit draw
   m.keep_scale = (float)(1.0 / (1.0 - p->dropout_p));
   m.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
   m.seed_hi = (uint32_t)(p->seed >> 32);

@@ -67,21 +67,12 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
                                                const float* sLq, const float* sDq, int g, int b,
                                                int h, int q0, int key, e16x8& pa0, e16x8& pa1,
                                                e16x8& da0, e16x8& da1) {
-  // Dropout: keys across lanes, so the four lanes of a quad hold the four keys
-  // of one Philox block.  Lane t of the quad draws the blocks of the rows
-  // with e = t (one per rr: bits 4 rr .. 4 rr + 3), and the quad shares them.
-  uint32_t kq[4] = {0xFFFFu, 0xFFFFu, 0xFFFFu, 0xFFFFu};
-  const int t = key & 3;
-  if (GENERAL && DROPOK && a.m.dropout) {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      mine |= dropout_keep4(a.m, b, h, q0 + 8 * rr + 4 * g + t, key & ~3) << (4 * rr);
-    kq[0] = __builtin_amdgcn_mov_dpp((int)mine, 0x00, 0xF, 0xF, false);  // quad_perm [0,0,0,0]
-    kq[1] = __builtin_amdgcn_mov_dpp((int)mine, 0x55, 0xF, 0xF, false);  // quad_perm [1,1,1,1]
-    kq[2] = __builtin_amdgcn_mov_dpp((int)mine, 0xAA, 0xF, 0xF, false);  // quad_perm [2,2,2,2]
-    kq[3] = __builtin_amdgcn_mov_dpp((int)mine, 0xFF, 0xF, 0xF, false);  // quad_perm [3,3,3,3]
-  }
+  // Dropout: keys across lanes, so the eight lanes of a Philox block share
+  // each row's block (bit 8 rr + t of kq[e]: row 8 rr + 4 g + e; t: the
+  // key's position in its block)
+  uint32_t kq[4] = {~0u, ~0u, ~0u, ~0u};
+  const int t = dropout_pos(key);
+  if (GENERAL && DROPOK && a.m.dropout) dropout_keep_octet(a.m, b, h, q0, g, key, kq);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
@@ -97,7 +88,7 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
         p = visible(a.m, qi, key) ? p : 0.f;
         pdrop = p;
         if (DROPOK && a.m.dropout) {
-          const bool keep = (kq[e] >> (4 * rr + t)) & 1u;
+          const bool keep = (kq[e] >> (8 * rr + t)) & 1u;
           pdrop = keep ? p : 0.f;  // 1 / (1 - p) is applied to dV at the store
           dpv = keep ? dpv * a.m.keep_scale : 0.f;
         }
@@ -133,20 +124,12 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
 #pragma unroll
   for (int t = 0; t < KT; ++t) sacc = mfma32x32x16(load8(qrow + 16 * t), load8(kr + 16 * t), sacc);
   mid();
-  // dropout keep bits: lane t of a quad draws the blocks of rows e = t and the
-  // quad shares them (keys lie across lanes, four per block)
+  // dropout keep bits: the eight lanes of a Philox block share each row's
+  // block (bit 8 rr + kt8 of kq[e]: row qs + 8 rr + 4 g + e; kt8: the key's
+  // position in its block)
   uint32_t kq[4] = {0u, 0u, 0u, 0u};
-  const int kt4 = key & 3;
-  if (DROP) {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      mine |= dropout_keep4(a.m, b, h, qs + 8 * rr + 4 * g + kt4, key & ~3) << (4 * rr);
-    kq[0] = __builtin_amdgcn_mov_dpp((int)mine, 0x00, 0xF, 0xF, false);  // quad_perm [0,0,0,0]
-    kq[1] = __builtin_amdgcn_mov_dpp((int)mine, 0x55, 0xF, 0xF, false);  // quad_perm [1,1,1,1]
-    kq[2] = __builtin_amdgcn_mov_dpp((int)mine, 0xAA, 0xF, 0xF, false);  // quad_perm [2,2,2,2]
-    kq[3] = __builtin_amdgcn_mov_dpp((int)mine, 0xFF, 0xF, 0xF, false);  // quad_perm [3,3,3,3]
-  }
+  const int kt8 = dropout_pos(key);
+  if (DROP) dropout_keep_octet(a.m, b, h, qs, g, key, kq);
   f32x16 dpacc = f32x16{};
 #pragma unroll
   for (int t = 0; t < KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), load8(vr + 16 * t), dpacc);
@@ -162,7 +145,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
       p[r] = fast_exp2(sacc[r] * a.scale_log2 - l4[e]);
-      const bool keep = !DROP || ((kq[e] >> (4 * rr + kt4)) & 1u);
+      const bool keep = !DROP || ((kq[e] >> (8 * rr + kt8)) & 1u);
       pa[r >> 3][r & 7] = (e16)(DROP ? (keep ? p[r] : 0.f) : p[r]);  // 1 / (1 - p) at the dV store
     }
   }
@@ -181,7 +164,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
       float dpv = dpacc[r];
-      if (DROP) dpv = ((kq[e] >> (4 * rr + kt4)) & 1u) ? dpv * a.m.keep_scale : 0.f;
+      if (DROP) dpv = ((kq[e] >> (8 * rr + kt8)) & 1u) ? dpv * a.m.keep_scale : 0.f;
       da[r >> 3][r & 7] = (e16)(p[r] * (dpv - d4[e]));
     }
   }
@@ -803,11 +786,12 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
       f32x16 st, dpt;
       sdp(buf, st, dpt);
       e16x8 d0, d1;
+      // this lane's keys ks + 8 rr + 4 g + (0..3) at bits 4 rr + (0..3)
+      const uint32_t kp = DROP ? dropout_keep_lane(a.m, b, h, myq, ks, g) : ~0u;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        // keys j4 .. j4 + 3 of this lane's query share one dropout block
         const int j4 = ks + 8 * rr + 4 * g;
-        const uint32_t keep = DROP ? dropout_keep4(a.m, b, h, myq, j4) : 0xFu;
+        const uint32_t keep = (kp >> (4 * rr)) & 0xFu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
@@ -830,9 +814,10 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
   auto fast_range = [&](auto drop) {
     constexpr bool FDROP = decltype(drop)::value;
     auto ds_of = [&](int j, const f32x16& st, const f32x16& dpt, e16x8& d0, e16x8& d1) {
+      const uint32_t kp = FDROP ? dropout_keep_lane(a.m, b, h, myq, j * C::BK, g) : ~0u;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const uint32_t keep = FDROP ? dropout_keep4(a.m, b, h, myq, j * C::BK + 8 * rr + 4 * g) : 0xFu;
+        const uint32_t keep = (kp >> (4 * rr)) & 0xFu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;

@@ -77,7 +77,7 @@ struct MaskArgs {
   const int* cu_q;    // varlen: sequence b has rows [cu_q[b], cu_q[b+1]) of the packed
   const int* cu_k;    //   query tensors and [cu_k[b], cu_k[b+1]) of the key ones; else null
   int dropout;        // 0/1
-  uint32_t keep_threshold;  // keep iff the Philox word >= threshold
+  uint32_t keep_threshold;  // keep iff the 16-bit Philox draw >= threshold
   float keep_scale;         // 1 / (1 - p)
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
 };
@@ -193,22 +193,70 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return u32x4{c0, c1, c2, c3};
 }
 
-// Dropout keep bits of keys j4 .. j4 + 3 (j4 a multiple of 4) in row i of
-// head (b, h): one Philox block per four consecutive keys, counter
-// (off_lo, off_hi, (i << 16) | j4, (b << 16) | h), key j4 + k kept iff word
-// k >= threshold.  Bit k of the result is key j4 + k.
-__device__ __forceinline__ uint32_t dropout_keep4(const MaskArgs& m, int b, int h, int i, int j4) {
-  const u32x4 x = philox4x32_10(m.off_lo, m.off_hi, ((uint32_t)i << 16) | (uint32_t)j4,
+// Dropout keep bits of one Philox block of row i of head (b, h): the block
+// at j0 (j0 % 16 = 0 or 4) serves keys j0 .. j0 + 3 and j0 + 8 .. j0 + 11
+// (positions 0 .. 7), counter (off_lo, off_hi, (i << 16) | j0,
+// (b << 16) | h); position q draws the 16-bit half q % 2 (low first) of
+// word q / 2 and is kept iff that draw >= threshold (ceil(p 2^16)).  Bit q
+// of the result is position q.  (Runs of four keys eight apart are what
+// one lane holds of a 32-key tile in the MFMA accumulator layout.)
+__device__ __forceinline__ uint32_t dropout_keep8(const MaskArgs& m, int b, int h, int i, int j0) {
+  const u32x4 x = philox4x32_10(m.off_lo, m.off_hi, ((uint32_t)i << 16) | (uint32_t)j0,
                                 ((uint32_t)b << 16) | (uint32_t)h, m.seed_lo, m.seed_hi);
   const uint32_t t = m.keep_threshold;
-  return (uint32_t)(x[0] >= t) | ((uint32_t)(x[1] >= t) << 1) | ((uint32_t)(x[2] >= t) << 2) |
-         ((uint32_t)(x[3] >= t) << 3);
+  uint32_t r = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    r |= ((uint32_t)((x[w] & 0xFFFFu) >= t) << (2 * w)) | ((uint32_t)((x[w] >> 16) >= t) << (2 * w + 1));
+  return r;
 }
 
 // Keep bit of one element (i, j).
 __device__ __forceinline__ bool dropout_keep(const MaskArgs& m, int b, int h, int i, int j) {
-  return (dropout_keep4(m, b, h, i, j & ~3) >> (j & 3)) & 1u;
+  const int j0 = (j & ~15) | (j & 4), q = ((j >> 1) & 4) | (j & 3);
+  return (dropout_keep8(m, b, h, i, j0) >> q) & 1u;
 }
+
+// Keep bits of this lane's keys of a 32-key tile (j0 % 32 = 0) of row i
+// when the lane holds keys j0 + 8 rr + 4 g + (0..3), rr = 0..3 (lane half
+// g): exactly the two blocks at j0 + 4 g and j0 + 16 + 4 g.  Bit 4 rr + e
+// is key j0 + 8 rr + 4 g + e.
+__device__ __forceinline__ uint32_t dropout_keep_lane(const MaskArgs& m, int b, int h, int i, int j0,
+                                                      int g) {
+  return dropout_keep8(m, b, h, i, j0 + 4 * g) | (dropout_keep8(m, b, h, i, j0 + 16 + 4 * g) << 8);
+}
+
+// Word e of a key octet's trade (dropout_keep_octet): QP broadcasts quad
+// lane e's draws to its quad; a rotation by eight lanes (DPP row_ror:8) of
+// that brings the other quad's lane e.  The quad with key bit 3 clear drew
+// rr = 0, 1, the other rr = 2, 3; byte rr of the result is row rr's block.
+template <int QP>
+__device__ __forceinline__ uint32_t octet_trade(uint32_t mine, int hq) {
+  const uint32_t own = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, QP, 0xF, 0xF, false);
+  const uint32_t oth = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0x128, 0xF, 0xF, false);
+  return hq ? (oth | (own << 16)) : (own | (oth << 16));
+}
+
+// Keep bits of a 32-query x 32-key tile whose keys lie across lanes (this
+// lane: key `key`, lane half g) and whose rows q0 + 8 rr + 4 g + e lie
+// inside the lane.  The eight lanes of a block (two quads eight lanes
+// apart) share each row's Philox block: the lane with key bit 3 = hq and
+// key % 4 = e draws rows rr = 2 hq and 2 hq + 1, and the eight trade them.
+// Bit 8 rr + (the key's position in its block) of kq[e] is the keep bit of
+// row q0 + 8 rr + 4 g + e.  Every lane of the wave must call it.
+__device__ __forceinline__ void dropout_keep_octet(const MaskArgs& m, int b, int h, int q0, int g,
+                                                   int key, uint32_t (&kq)[4]) {
+  const int hq = (key >> 3) & 1, j0 = (key & ~15) | (key & 4);
+  const int row = q0 + 16 * hq + 4 * g + (key & 3);  // rr = 2 hq
+  const uint32_t mine = dropout_keep8(m, b, h, row, j0) | (dropout_keep8(m, b, h, row + 8, j0) << 8);
+  kq[0] = octet_trade<0x00>(mine, hq);  // quad_perm [0,0,0,0]
+  kq[1] = octet_trade<0x55>(mine, hq);  // quad_perm [1,1,1,1]
+  kq[2] = octet_trade<0xAA>(mine, hq);  // quad_perm [2,2,2,2]
+  kq[3] = octet_trade<0xFF>(mine, hq);  // quad_perm [3,3,3,3]
+}
+
+// Position of key `key` in its Philox block (bit index in dropout_keep8).
+__device__ __forceinline__ int dropout_pos(int key) { return ((key >> 1) & 4) | (key & 3); }
 
 // Address of row `row` (0 <= row < 2^31) of one head whose rows are `rs`
 // bytes apart (rs < 2^32): a single 32 x 32 -> 64-bit multiply-add.

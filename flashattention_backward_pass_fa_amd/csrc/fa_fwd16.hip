@@ -190,10 +190,11 @@ __global__ void __launch_bounds__(FCfg<D>::NT, FCfg<D>::MINB) fwd_kernel(FwdArgs
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      // this lane's keys k0 + 32 kt + 8 rr + 4 g + (0..3) at bits 4 rr + (0..3)
+      const uint32_t kp = DROP ? dropout_keep_lane(a.m, b, h, myq, k0 + 32 * kt, g) : ~0u;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        // keys j4 .. j4 + 3 of this lane's query share one dropout block
-        const uint32_t keep = DROP ? dropout_keep4(a.m, b, h, myq, k0 + 32 * kt + 8 * rr + 4 * g) : 0xFu;
+        const uint32_t keep = (kp >> (4 * rr)) & 0xFu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;

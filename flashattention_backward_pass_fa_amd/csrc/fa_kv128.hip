@@ -16,25 +16,16 @@ namespace {
 // tile from its S = Q K^T and dP = dO V^T accumulators (keys across lanes,
 // queries inside the lane: element r of lane l is query q0 + 8 (r / 4) +
 // 4 g + r % 4, key `key`).  MASK zeroes hidden pairs; DROP applies the keep
-// mask, one Philox block per four keys shared by the lanes of a quad.
+// mask, one Philox block per eight keys shared by the eight lanes holding them.
 // sDq holds -D.  Returns the values as four runs of 4 consecutive queries
 // (rr = 0..3).
 template <bool MASK, bool DROP>
 __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const f32x16& dp,
                                         const float* sLq, const float* sDq, int g, int b, int h,
                                         int q0, int key, e16x4 (&pw)[4], e16x4 (&dw)[4]) {
-  uint32_t kq[4] = {0xFFFFu, 0xFFFFu, 0xFFFFu, 0xFFFFu};
-  const int t = key & 3;
-  if (DROP) {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      mine |= dropout_keep4(a.m, b, h, q0 + 8 * rr + 4 * g + t, key & ~3) << (4 * rr);
-    kq[0] = __builtin_amdgcn_mov_dpp((int)mine, 0x00, 0xF, 0xF, false);  // quad_perm [0,0,0,0]
-    kq[1] = __builtin_amdgcn_mov_dpp((int)mine, 0x55, 0xF, 0xF, false);  // quad_perm [1,1,1,1]
-    kq[2] = __builtin_amdgcn_mov_dpp((int)mine, 0xAA, 0xF, 0xF, false);  // quad_perm [2,2,2,2]
-    kq[3] = __builtin_amdgcn_mov_dpp((int)mine, 0xFF, 0xF, 0xF, false);  // quad_perm [3,3,3,3]
-  }
+  uint32_t kq[4] = {~0u, ~0u, ~0u, ~0u};
+  const int t = dropout_pos(key);
+  if (DROP) dropout_keep_octet(a.m, b, h, q0, g, key, kq);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
@@ -47,7 +38,7 @@ __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const
       float dpv = dp[r];
       float pk = p;
       if (DROP) {
-        const bool keep = (kq[e] >> (4 * rr + t)) & 1u;
+        const bool keep = (kq[e] >> (8 * rr + t)) & 1u;
         pk = keep ? p : 0.f;  // 1 / (1 - p) is applied to dV at the store
         dpv = keep ? dpv * a.m.keep_scale : 0.f;
       }

@@ -109,14 +109,16 @@ typedef struct fa_tensor {
  *                 (with Nq = Nk and windows >= 0 key i is always visible;
  *                 with Nq > Nk, or a window that misses [0, Nk), a row can
  *                 see no key)
- *   dropout_p     probability of dropping an attention weight, in [0, 1);
- *                 kept weights are scaled by 1/(1 - p).  Requires B, H, Nq,
- *                 Nk <= 65536 when p > 0.
+ *   dropout_p     probability of dropping an attention weight, in
+ *                 [0, 1 - 2^-16]; kept weights are scaled by 1/(1 - p).
+ *                 Requires B, H, Nq, Nk <= 65536 when p > 0.
  *   seed, offset  Philox4x32-10 stream of the dropout mask: key = seed,
- *                 one block per four keys j4 = j - j % 4, counter =
- *                 (offset, (i << 16) | j4, (b << 16) | h); weight
- *                 (b, h, i, j) is kept iff word j % 4 >= ceil(p * 2^32);
- *                 i and j count from the start of the sequence.
+ *                 one block per eight keys j8 = j - j % 8, counter =
+ *                 (offset, (i << 16) | j8, (b << 16) | h); weight
+ *                 (b, h, i, j) draws the 16-bit half j % 2 (low first) of
+ *                 word (j % 8) / 2 and is kept iff that draw >=
+ *                 ceil(p * 2^16) (kept with probability within 2^-16 of
+ *                 1 - p); i and j count from the start of the sequence.
  *   deterministic non-zero: dQ by a separate Q-outer kernel, bit-identical
  *                 run to run; zero: for bf16/fp16, dQ by fp32 atomics into
  *                 a workspace (fp32 computes dQ without atomics either way).

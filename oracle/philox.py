@@ -8,14 +8,21 @@ section "Dropout": the kernel draws a Bernoulli keep mask from a Philox
 generator seeded by (seed, offset), and a checker must draw the same mask.
 The page gives no mapping from (seed, offset, element) to Philox words, so
 this oracle fixes one: the seed is the key, the offset the low counter
-words, the element the high ones.  Each Philox block serves four
-consecutive keys of one row:
+words, the element the high ones.  Each Philox block (128 bits) serves
+eight keys of one row, 16 bits each: two runs of four keys eight apart,
+j0 .. j0 + 3 and j0 + 8 .. j0 + 11 with j0 = 16 m or 16 m + 4 (so a block of
+16 consecutive keys is served by two Philox blocks).  For key j:
 
+    j0      = (j - j mod 16) + (j mod 8 - j mod 4)    (the block's first key)
+    pos     = 4 * ((j mod 16) div 8) + j mod 4       (0 .. 7 within the block)
     key     = (low 32 bits of seed, high 32 bits of seed)
     counter = (low 32 bits of offset, high 32 bits of offset,
-               (i << 16) | (j - j mod 4), (b << 16) | h)
-    x       = word (j mod 4) of Philox4x32-10(counter, key)
-    keep    = x >= T,  T = ceil(p * 2**32)   (exactly x / 2**32 >= p)
+               (i << 16) | j0, (b << 16) | h)
+    w       = word (pos div 2) of Philox4x32-10(counter, key)
+    x       = the low 16 bits of w for even pos, the high 16 bits for odd pos
+    keep    = x >= T,  T = ceil(p * 2**16)   (exactly x / 2**16 >= p)
+
+so a key is kept with probability 1 - T / 2**16, within 2**-16 of 1 - p.
 
 The block function is Philox4x32 with 10 rounds as published by Salmon,
 Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11):
@@ -63,20 +70,20 @@ def philox4x32_10(counter, key, rounds=10):
 
 
 def keep_threshold(p):
-    """Integer threshold T = ceil(p * 2**32); keep iff the 32-bit draw >= T.
+    """Integer threshold T = ceil(p * 2**16); keep iff the 16-bit draw >= T.
 
-    p * 2**32 is exact in binary64 (a power-of-two scaling), so T is exact.
+    p * 2**16 is exact in binary64 (a power-of-two scaling), so T is exact.
     """
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must lie in [0, 1)")
-    t = math.ceil(p * 4294967296.0)
-    if t > 0xFFFFFFFF:
+    t = math.ceil(p * 65536.0)
+    if t > 0xFFFF:
         raise ValueError("dropout probability too close to 1")
     return t
 
 
 def dropout_uniform_bits(seed, offset, b, h, rows, cols):
-    """The 32-bit draw x for every (i, j) in rows x cols of head (b, h)."""
+    """The 16-bit draw x for every (i, j) in rows x cols of head (b, h)."""
     rows = _u64(rows).reshape(-1, 1)
     cols = _u64(cols).reshape(1, -1)
     if (rows.size and rows.max() >= 65536) or (cols.size and cols.max() >= 65536):
@@ -86,8 +93,10 @@ def dropout_uniform_bits(seed, offset, b, h, rows, cols):
     seed = int(seed)
     offset = int(offset)
     key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    group = cols & ~np.uint64(3)          # first key of the four that share a block
-    word = (cols & np.uint64(3)).astype(np.int64)
+    group = (cols & ~np.uint64(15)) | (cols & np.uint64(4))   # j0, the block's first key
+    pos = ((cols >> np.uint64(1)) & np.uint64(4)) | (cols & np.uint64(3))
+    word = (pos >> np.uint64(1)).astype(np.int64)
+    half = (pos & np.uint64(1)) * np.uint64(16)   # bit position of the key's half
     w2 = (rows << np.uint64(16)) | group
     w3 = np.uint64((int(b) << 16) | int(h))
     shape = w2.shape
@@ -99,7 +108,8 @@ def dropout_uniform_bits(seed, offset, b, h, rows, cols):
     )
     words = np.stack(philox4x32_10(counter, key))       # [4, rows, cols]
     word = np.broadcast_to(word, shape)
-    return np.take_along_axis(words, word[None], axis=0)[0]
+    w = np.take_along_axis(words, word[None], axis=0)[0].astype(np.uint64)
+    return ((w >> np.broadcast_to(half, shape)) & np.uint64(0xFFFF)).astype(np.uint32)
 
 
 def dropout_keep(seed, offset, b, h, rows, cols, p):

@@ -5,8 +5,10 @@ PyTorch's header-only engine (compiled with g++) and rocRAND's (compiled
 with hipcc for the host).  Both are built and run at test time; no output of
 theirs is stored.  Their stream (seed, subsequence, offset) places the seed
 in the key and (offset, subsequence) in the counter words, which is the
-mapping the dropout mask uses with subsequence = (b<<48)|(h<<32)|(i<<16)|j4,
-j4 = j - j mod 4: key j takes word j mod 4 of that block.
+mapping the dropout mask uses with subsequence = (b<<48)|(h<<32)|(i<<16)|j0,
+j0 = 16 m or 16 m + 4: the block serves keys j0 .. j0 + 3 and j0 + 8 .. j0 + 11
+at positions 0 .. 7, position q taking the 16-bit half q mod 2 (low half
+first) of word q div 2.
 """
 
 import os
@@ -50,8 +52,8 @@ def _cases():
     seeds = [0, 1, 0x5EED, 0xFFFFFFFF, 1 << 32, (1 << 64) - 1]
     seeds += [int(x) for x in rng.integers(0, 2**63, 4)]
     offsets = [0, 1, 0xFFFFFFFF, 1 << 32, (1 << 40) + 12345]
-    coords = [(0, 0, 0, 0), (65535, 65535, 65535, 65532), (1, 2, 3, 4), (3, 15, 8191, 7000),
-              (65535, 65535, 65535, 65535), (1, 2, 3, 5)]
+    coords = [(0, 0, 0, 0), (65535, 65535, 65535, 65524), (1, 2, 3, 16), (3, 15, 8191, 7008),
+              (65535, 65535, 65535, 65535), (1, 2, 3, 5), (1, 2, 3, 4), (7, 8, 9, 65520)]
     coords += [tuple(int(x) for x in rng.integers(0, 65536, 4)) for _ in range(6)]
     coords += [tuple(int(x) for x in rng.integers(0, 65536, 3)) + (4 * int(rng.integers(0, 16384)),)
                for _ in range(6)]
@@ -82,22 +84,27 @@ def test_block_function_matches_witness(witness):
         key = (seed & 0xFFFFFFFF, seed >> 32)
         got = [int(w) for w in oracle.philox4x32_10(counter, key)]
         assert got == words, (seed, off, b, h, i, j)
-        if j % 4 == 0:
-            # the block of keys j .. j + 3: key j + k draws word k
-            cols = [c for c in range(j, j + 4) if c < 65536]
+        if j % 16 in (0, 4):
+            # the block of keys j .. j + 3, j + 8 .. j + 11: position q draws
+            # the 16-bit half q mod 2 (low first) of word q div 2
+            cols = [j + q for q in range(4)] + [j + 8 + q for q in range(4)]
             x = oracle.dropout_uniform_bits(seed, off, b, h, [i], cols)[0]
-            assert [int(v) for v in x] == words[:len(cols)], (seed, off, b, h, i, j)
+            halves = [(w >> (16 * k)) & 0xFFFF for w in words for k in range(2)]
+            assert [int(v) for v in x] == halves, (seed, off, b, h, i, j)
 
 
 def test_keep_threshold_is_exact():
     assert oracle.keep_threshold(0.0) == 0
-    assert oracle.keep_threshold(0.1) == 429496730          # ceil(0.1 * 2**32)
-    assert oracle.keep_threshold(0.5) == 1 << 31
+    assert oracle.keep_threshold(0.1) == 6554               # ceil(0.1 * 2**16)
+    assert oracle.keep_threshold(0.5) == 1 << 15
+    assert oracle.keep_threshold(1 - 2**-16) == 0xFFFF
     with pytest.raises(ValueError):
         oracle.keep_threshold(1.0)
-    # x >= T  <=>  x / 2**32 >= p, checked at the boundary
+    with pytest.raises(ValueError):
+        oracle.keep_threshold(1 - 2**-17)                   # T would be 2**16
+    # x >= T  <=>  x / 2**16 >= p, checked at the boundary
     t = oracle.keep_threshold(0.1)
-    assert (t - 1) / 2**32 < 0.1 <= t / 2**32
+    assert (t - 1) / 2**16 < 0.1 <= t / 2**16
 
 
 def test_keep_fraction_and_uniformity():
@@ -107,8 +114,13 @@ def test_keep_fraction_and_uniformity():
     frac = keep.mean()
     sigma = np.sqrt(0.1 * 0.9 / keep.size)
     assert abs(frac - 0.9) < 6 * sigma
-    # chi-square of the top byte against uniform (255 dof; 6 sigma ~ 391)
-    counts = np.bincount((x >> 24).astype(np.int64), minlength=256)
+    # chi-square of the top byte of the 16-bit draw against uniform (255
+    # dof; 6 sigma ~ 391), and of the low byte
+    counts = np.bincount((x >> 8).astype(np.int64), minlength=256)
+    expected = x.size / 256
+    chi2 = ((counts - expected) ** 2 / expected).sum()
+    assert chi2 < 255 + 6 * np.sqrt(2 * 255)
+    counts = np.bincount((x & 0xFF).astype(np.int64), minlength=256)
     expected = x.size / 256
     chi2 = ((counts - expected) ** 2 / expected).sum()
     assert chi2 < 255 + 6 * np.sqrt(2 * 255)
@@ -122,13 +134,22 @@ def test_mask_changes_with_offset_and_head():
     assert (a != b).mean() > 0.1 and (a != c).mean() > 0.1
 
 
-def test_words_of_one_block_serve_four_keys():
-    """Keys 4m .. 4m + 3 of a row share one block; the next four use the next block."""
+def test_words_of_one_block_serve_eight_keys():
+    """Keys 16 m + 4 t + (0..3) and 16 m + 8 + 4 t + (0..3) of a row (t = 0, 1)
+    share one block, two per word (low half first); every key of the row is
+    served by exactly one block position."""
     rows = np.arange(5)
     cols = np.arange(64)
     x = oracle.dropout_uniform_bits(0x5EED, 7, 2, 9, rows, cols)
     for i in rows:
-        for m in range(16):
-            counter = (7, 0, (int(i) << 16) | (4 * m), (2 << 16) | 9)
-            words = [int(w) for w in oracle.philox4x32_10(counter, (0x5EED, 0))]
-            assert [int(v) for v in x[i, 4 * m:4 * m + 4]] == words
+        seen = np.zeros(64, dtype=int)
+        for m in range(4):
+            for t in range(2):
+                j0 = 16 * m + 4 * t
+                counter = (7, 0, (int(i) << 16) | j0, (2 << 16) | 9)
+                words = [int(w) for w in oracle.philox4x32_10(counter, (0x5EED, 0))]
+                halves = [w & 0xFFFF if k % 2 == 0 else w >> 16 for w in words for k in range(2)]
+                keys = [j0 + q for q in range(4)] + [j0 + 8 + q for q in range(4)]
+                assert [int(v) for v in x[i, keys]] == halves
+                seen[keys] += 1
+        assert (seen == 1).all()
