@@ -69,27 +69,56 @@ __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const
 template <int D>
 struct KvSCfg {
   static constexpr int BC = 128, BR = 64, NT = 512;
-  static constexpr int LD = lds_stride(D);  // Q, dO tiles (row-major, padded)
   // P~ and dS tiles, [key][query]: 72 elements = 36 dwords per row, an odd
   // multiple of 4 modulo 64, so the 16-byte A-operand reads of 16 lanes
   // (16 consecutive keys) fall on disjoint banks
   static constexpr int LDP = BR + 8;
-  static constexpr int KT = D / 16, CH = D / 8;
-  static constexpr int LOADS = BR * CH / NT;  // Q (and dO) chunks per thread per block
+  static constexpr int KT = D / 16;
+  static constexpr int TILE = BR * D;  // one unpadded Q or dO tile (16 KB)
+  // 1 KB LDS-DMA pieces of a Q, dO tile pair per consumer wave
+  static constexpr int PIECES = 2 * TILE * 2 / 1024 / 4;
 };
+
+// Q and dO tiles are stored unpadded (LDS-DMA writes whole 1 KB pieces, so
+// rows cannot be padded) with 16-byte chunk k of row r in slot
+// k ^ tile_swz(r) of that row.  The swizzle, a bijection on r % 16, keeps
+// both reads conflict-free on gfx950's 64 banks: 16 lanes reading one chunk
+// of 16 consecutive rows, and the transposed 8-byte reads of 4 consecutive
+// rows x 4 consecutive chunks.
+__device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// One 16-byte-per-lane LDS-DMA: lane l's 16 bytes at src land at LDS byte
+// address lds + 16 l (lds wave-uniform).  Written as assembly so that the
+// compiler, which cannot tell these LDS writes from later LDS reads, does
+// not wait for the request before every one of them; the issuing wave
+// waits (vmcnt) before the barrier that publishes the data.  The request
+// has no register result, and the compiler's own vmcnt waits stay correct
+// (an extra outstanding request only makes them wait longer).  No code in
+// this file uses M0 otherwise; one wait state is needed between writing M0
+// and the request.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 template <int D, bool DROP>
 __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
   static_assert(D == 128, "four 32-column slices per matrix: one per consumer wave");
   using C = KvSCfg<D>;
-  constexpr int TILE = C::BR * C::LD, PT = C::BC * C::LDP;
-  // [0, 4 TILE): Q, dO double buffers; then two P~ / dS buffer pairs; all of
-  // it reused for staging the output rows after the loop
+  constexpr int TILE = C::TILE, PT = C::BC * C::LDP;
+  // [0, 4 TILE): Q, dO tiles of two blocks (Q then dO per block); then two
+  // P~ / dS buffer pairs; all of it reused for staging the output rows after
+  // the loop
   __shared__ __attribute__((aligned(16))) e16 smem[4 * TILE + 4 * PT];
   __shared__ __attribute__((aligned(16))) float sL[2][C::BR];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BR];
-  auto sQ = [&](int buf) { return smem + buf * TILE; };
-  auto sO = [&](int buf) { return smem + (2 + buf) * TILE; };
+  auto sQ = [&](int buf) { return smem + 2 * buf * TILE; };
+  auto sO = [&](int buf) { return smem + (2 * buf + 1) * TILE; };
   auto sP = [&](int buf) { return smem + 4 * TILE + 2 * buf * PT; };
   auto sS = [&](int buf) { return smem + 4 * TILE + (2 * buf + 1) * PT; };
 
@@ -115,29 +144,29 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
   const char* q_head = (const char*)at<e16>(a.q, b, h, 0);
   const char* o_head = (const char*)at<e16>(a.dout, b, h, 0);
   const uint32_t q_rs = (uint32_t)a.q.sn * 2, o_rs = (uint32_t)a.dout.sn * 2;
-  e16x8 pq[C::LOADS], po[C::LOADS];
-  float pld = 0.f;
-  auto load_tile = [&](int it) {
-    const int q0 = it * C::BR;
+  // Block it's Q and dO rows into tile buffer buf by LDS-DMA (consumer
+  // waves): consumer `role` moves PIECES 1 KB pieces of four rows (pieces
+  // 0..15: Q, 16..31: dO); lane l of a piece fetches, for row 4 p + l / 16,
+  // the chunk that belongs in slot l % 16.  Rows past the end read the last
+  // row (finite; every use of them is masked or never stored).
+  auto dma_tile = [&](int it, int buf) {
 #pragma unroll
-    for (int x = 0; x < C::LOADS; ++x) {
-      const int chunk = tid + x * C::NT;
-      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      const int qr = min(q0 + row, NQ - 1);  // rows past the end are masked: read a valid one
-      pq[x] = load8((const e16*)row_addr(q_head, q_rs, qr) + col);
-      po[x] = load8((const e16*)row_addr(o_head, o_rs, qr) + col);
+    for (int x = 0; x < C::PIECES; ++x) {
+      const int piece = C::PIECES * role + x;
+      const int mat = piece >> 4, grp = piece & 15;
+      const int row = 4 * grp + (lane >> 4);
+      const int chunk = (lane & 15) ^ tile_swz(row);
+      const char* src = row_addr(mat ? o_head : q_head, mat ? o_rs : q_rs, min(it * C::BR + row, NQ - 1)) + 16 * chunk;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_address(smem + (2 * buf + mat) * TILE + 512 * grp)));
     }
-    if (tid < 2 * C::BR)
-      pld = (tid < C::BR ? a.lse : a.delta)[row_base + min(q0 + (tid & (C::BR - 1)), NQ - 1)];
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < C::LOADS; ++x) {
-      const int chunk = tid + x * C::NT;
-      const int row = chunk / C::CH, col = (chunk % C::CH) * 8;
-      store8(sQ(buf) + row * C::LD + col, pq[x]);
-      store8(sO(buf) + row * C::LD + col, po[x]);
-    }
+  // L (as L log2 e) and -D of one block, moved by waves 0 and 1
+  float pld = 0.f;
+  auto ld_load = [&](int it) {
+    if (tid < 2 * C::BR)
+      pld = (tid < C::BR ? a.lse : a.delta)[row_base + min(it * C::BR + (tid & (C::BR - 1)), NQ - 1)];
+  };
+  auto ld_store = [&](int buf) {
     if (tid < C::BR) sL[buf][tid] = pld * kLog2e;
     else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = -pld;  // -D: the start value of dP - D
   };
@@ -160,12 +189,15 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
   // The two roles run separate copies of the loop (so that neither holds the
   // other's registers) with the same barriers in the same order.  Iteration
   // it: consumers take block it (tile and P~/dS buffer (it - it0) & 1),
-  // producers block it + 1 (the other ones); then every thread stores block
-  // it + 2's Q, dO (loaded during the iteration) into the tile block it used.
-  // The first iteration is preceded by block it0's Q, dO and P~, dS, and
-  // block it0 + 1's Q, dO.
+  // producers block it + 1 (the other ones).  Block it's tile is dead by then
+  // (the producers formed block it, and the consumers read their B operands
+  // of it, during the iteration before), so the consumers request block
+  // it + 2's Q, dO into it at the top of the iteration and wait for them
+  // before its barrier, and waves 0 and 1 store block it + 2's L and D.  The
+  // first iteration is preceded by the two first tiles and the producers'
+  // pass over block it0.
   if (producer) {
-    if (it0 < it1) load_tile(it0);
+    if (it0 < it1) ld_load(it0);
     // K and V rows: B operands of S and dP, in registers for the whole loop
     e16x8 kreg[C::KT], vreg[C::KT];
     {
@@ -177,17 +209,20 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
         vreg[t] = load8(vp + 16 * t + 8 * g);
       }
     }
-    if (it0 < it1) store_tile(0);
+    if (it0 < it1) ld_store(0);
     // K and V must have landed before the loop: the wait counter cannot tell
     // them from later prefetches, so a register still pending here would
     // make every iteration wait for its own prefetch.
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     lds_barrier();
+    // A operand of k-step t: row c of a half, chunk 2 t + g (elements from
+    // the half's first row; rows 32 qh + c share c's swizzle)
+    int aoff[C::KT];
+#pragma unroll
+    for (int t = 0; t < C::KT; ++t) aoff[t] = c * D + 8 * ((2 * t + g) ^ tile_swz(c));
     // P~ and dS of block it (both 32-query halves) into buffer pb
     auto produce = [&](int it, int qb, int pb, auto full) {
       constexpr bool FULL = decltype(full)::value;
-      const e16* Qs = sQ(qb);
-      const e16* Os = sO(qb);
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         const int qs = it * C::BR + 32 * qh;
@@ -205,12 +240,11 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
           continue;
         }
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
-        const e16* qrow = Qs + (32 * qh + c) * C::LD + 8 * g;
-        const e16* orow = Os + (32 * qh + c) * C::LD + 8 * g;
+        const e16* qa = sQ(qb) + 32 * qh * D;
 #pragma unroll
-        for (int t = 0; t < C::KT; ++t) sacc = mfma32x32x16(load8(qrow + 16 * t), kreg[t], sacc);
+        for (int t = 0; t < C::KT; ++t) sacc = mfma32x32x16(load8(qa + aoff[t]), kreg[t], sacc);
 #pragma unroll
-        for (int t = 0; t < C::KT; ++t) dpacc = mfma32x32x16(load8(orow + 16 * t), vreg[t], dpacc);
+        for (int t = 0; t < C::KT; ++t) dpacc = mfma32x32x16(load8(qa + TILE + aoff[t]), vreg[t], dpacc);
         e16x4 pw[4], dw[4];
         const float* sLq = &sL[qb][32 * qh];
         const float* sDq = &sD[qb][32 * qh];
@@ -232,12 +266,11 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
     // this order.
     auto produce_full = [&](int it, int qb, int pb) {
       constexpr int AHEAD = 4;
-      const e16* qa = sQ(qb) + c * C::LD + 8 * g;
-      const e16* oa = sO(qb) + c * C::LD + 8 * g;
+      const e16* qa = sQ(qb);
       // product j: query half j / 16, S = Q K^T (j % 16 < 8) or dP = dO V^T,
       // k-step j % 8
       auto operand = [&](int j) {
-        return load8(((j & 15) < 8 ? qa : oa) + (j >> 4) * 32 * C::LD + 16 * (j & 7));
+        return load8(qa + ((j & 15) < 8 ? 0 : TILE) + (j >> 4) * 32 * D + aoff[j & 7]);
       };
       auto minus_d = [&](int half) {
         f32x16 v;
@@ -308,21 +341,18 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
       }
     };
     if (it0 < it1) {
-      if (it0 + 1 < it1) load_tile(it0 + 1);
+      if (it0 + 1 < it1) ld_load(it0 + 1);
       produce_any(it0, 0, 0);
-      if (it0 + 1 < it1) store_tile(1);
+      if (it0 + 1 < it1) ld_store(1);
       lds_barrier();
     }
     for (int it = it0; it < it1; ++it) {
       const int cur = (it - it0) & 1, nxt = cur ^ 1;
       const bool has_next2 = it + 2 < it1;
-      if (has_next2) load_tile(it + 2);
+      if (has_next2) ld_load(it + 2);
       if (it + 1 < it1) produce_any(it + 1, nxt, nxt);
+      if (has_next2) ld_store(cur);
       lds_barrier();
-      if (has_next2) {
-        store_tile(cur);
-        lds_barrier();
-      }
     }
   } else {
     const int n0 = 32 * role;  // this consumer's columns of dV and dK
@@ -333,44 +363,80 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
       acc_k[m] = f32x16{};
     }
     if (it0 < it1) {
-      load_tile(it0);
-      store_tile(0);
+      dma_tile(it0, 0);
+      if (it0 + 1 < it1) dma_tile(it0 + 1, 1);
     }
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
     lds_barrier();
-    // acc += A^T B over block it's queries, A = P~ (dV) or dS (dK) read
-    // key-major from buffer pb, B = dO or Q read transposed from tile qb
-    auto consume = [&](int qb, int pb) {
+    // B operands (dO and Q read transposed for this consumer's column slice)
+    // of the block being consumed, in registers: they are read from that
+    // block's tile during the iteration before, so a tile is dead once the
+    // producers have formed its block and the next tile can replace it
+    // during the iteration, with one barrier per block.
+    // Transposed reads of a swizzled tile: lane l gets rows 16 ks + 8 g +
+    // (0..3) (and + 4..7) of column n0 + l % 32 (the lane's 8-byte read: row
+    // r0 + j / 4, columns n0 + 16 ((l / 16) % 2) + 4 (j % 4) .. + 3, j = l % 16,
+    // which stay in one 16-byte chunk; rows 16 ks + r share r's swizzle).
+    int tro[2];
+    {
+      const int j = lane & 15;
+      const int chunk = (n0 >> 3) + 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int r = 8 * g + 4 * x + (j >> 2);
+        tro[x] = r * D + 8 * (chunk ^ tile_swz(r)) + 4 * (j & 1);
+      }
+    }
+    e16x8 bo_r[C::BR / 16], bq_r[C::BR / 16];
+    auto read_b = [&](int qb, int ks) {
+      const int ro = 16 * ks * D;
+      bo_r[ks] = concat(lds_read_tr(sO(qb) + ro + tro[0]), lds_read_tr(sO(qb) + ro + tro[1]));
+      bq_r[ks] = concat(lds_read_tr(sQ(qb) + ro + tro[0]), lds_read_tr(sQ(qb) + ro + tro[1]));
+    };
+    // acc += A^T B over a block's queries, A = P~ (dV) or dS (dK) read
+    // key-major from buffer pb; each k-step's B operands are then replaced by
+    // those of the next block (tile qn; after the last block that tile holds
+    // an older block, read but never used: no branch splits the loop)
+    // The A operands of k-step ks + 1 are requested before the products of
+    // k-step ks (two sets in flight), each step fenced.
+    auto consume = [&](int pb, int qn) {
       const e16* Pt = sP(pb);
       const e16* St = sS(pb);
-#pragma unroll
-      for (int ks = 0; ks < C::BR / 16; ++ks) {  // 16-query k-steps
-        const e16x8 bo = tr_operand(sO(qb), C::LD, 16 * ks + 8 * g, 16 * ks + 8 * g + 4, n0, lane);
-        const e16x8 bq = tr_operand(sQ(qb), C::LD, 16 * ks + 8 * g, 16 * ks + 8 * g + 4, n0, lane);
+      e16x8 pa[2][4], sa[2][4];
+      auto read_a = [&](int ks) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int off = (32 * m + c) * C::LDP + 16 * ks + 8 * g;
-          acc_v[m] = mfma32x32x16(load8(Pt + off), bo, acc_v[m]);
-          acc_k[m] = mfma32x32x16(load8(St + off), bq, acc_k[m]);
+          pa[ks & 1][m] = load8(Pt + off);
+          sa[ks & 1][m] = load8(St + off);
         }
+      };
+      read_a(0);
+#pragma unroll
+      for (int ks = 0; ks < C::BR / 16; ++ks) {  // 16-query k-steps
+        if (ks + 1 < C::BR / 16) read_a(ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc_v[m] = mfma32x32x16(pa[ks & 1][m], bo_r[ks], acc_v[m]);
+          acc_k[m] = mfma32x32x16(sa[ks & 1][m], bq_r[ks], acc_k[m]);
+        }
+        read_b(qn, ks);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (it0 < it1) {
-      if (it0 + 1 < it1) {
-        load_tile(it0 + 1);
-        store_tile(1);
-      }
+#pragma unroll
+      for (int ks = 0; ks < C::BR / 16; ++ks) read_b(0, ks);
       lds_barrier();
     }
     for (int it = it0; it < it1; ++it) {
-      const int cur = (it - it0) & 1;
+      const int cur = (it - it0) & 1, nxt = cur ^ 1;
       const bool has_next2 = it + 2 < it1;
-      if (has_next2) load_tile(it + 2);
-      consume(cur, cur);
+      if (has_next2) dma_tile(it + 2, cur);
+      consume(cur, nxt);
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
       lds_barrier();
-      if (has_next2) {
-        store_tile(cur);
-        lds_barrier();
-      }
     }
     // dK = sm_scale dS^T Q and dV = (Z o P)^T dO / (1 - p), rounded once to
     // the element type: each consumer writes its slices row-major into LDS
