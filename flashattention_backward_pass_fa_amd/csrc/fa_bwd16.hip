@@ -69,9 +69,9 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
                                                e16x8& da0, e16x8& da1) {
   // Dropout: keys across lanes, so the eight lanes of a Philox block share
   // each row's block (bit 8 rr + t of kq[e]: row 8 rr + 4 g + e; t: the
-  // key's position in its block)
+  // key's bit in a byte of the traded words)
   uint32_t kq[4] = {~0u, ~0u, ~0u, ~0u};
-  const int t = dropout_pos(key);
+  const int t = dropout_octet_bit(key);
   if (GENERAL && DROPOK && a.m.dropout) dropout_keep_octet(a.m, b, h, q0, g, key, kq);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -88,9 +88,9 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
         p = visible(a.m, qi, key) ? p : 0.f;
         pdrop = p;
         if (DROPOK && a.m.dropout) {
-          const bool keep = (kq[e] >> (8 * rr + t)) & 1u;
-          pdrop = keep ? p : 0.f;  // 1 / (1 - p) is applied to dV at the store
-          dpv = keep ? dpv * a.m.keep_scale : 0.f;
+          const uint32_t km = bit_mask(kq[e], 8 * rr + t);  // all ones iff kept
+          pdrop = masked(p, km);  // 1 / (1 - p) is applied to dV at the store
+          dpv = masked(dpv * a.m.keep_scale, km);
         }
       }
       const float ds = p * (dpv - d4[e]);
@@ -126,9 +126,9 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
   mid();
   // dropout keep bits: the eight lanes of a Philox block share each row's
   // block (bit 8 rr + kt8 of kq[e]: row qs + 8 rr + 4 g + e; kt8: the key's
-  // position in its block)
+  // bit in a byte of the traded words)
   uint32_t kq[4] = {0u, 0u, 0u, 0u};
-  const int kt8 = dropout_pos(key);
+  const int kt8 = dropout_octet_bit(key);
   if (DROP) dropout_keep_octet(a.m, b, h, qs, g, key, kq);
   f32x16 dpacc = f32x16{};
 #pragma unroll
@@ -137,6 +137,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
 #pragma unroll
   for (int n = 0; n < DT; ++n) b0[n] = tr_operand(Os, LD, ulo, ulo + 8, 32 * n, lane);
   float p[16];
+  uint32_t km[16];  // dropout: all ones for a kept element, zero for a dropped one
   e16x8 pa[2], da[2];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -145,8 +146,8 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
       p[r] = fast_exp2(sacc[r] * a.scale_log2 - l4[e]);
-      const bool keep = !DROP || ((kq[e] >> (8 * rr + kt8)) & 1u);
-      pa[r >> 3][r & 7] = (e16)(DROP ? (keep ? p[r] : 0.f) : p[r]);  // 1 / (1 - p) at the dV store
+      km[r] = DROP ? bit_mask(kq[e], 8 * rr + kt8) : ~0u;
+      pa[r >> 3][r & 7] = (e16)(DROP ? masked(p[r], km[r]) : p[r]);  // 1 / (1 - p) at the dV store
     }
   }
 #pragma unroll
@@ -164,7 +165,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
       float dpv = dpacc[r];
-      if (DROP) dpv = ((kq[e] >> (8 * rr + kt8)) & 1u) ? dpv * a.m.keep_scale : 0.f;
+      if (DROP) dpv = masked(dpv * a.m.keep_scale, km[r]);
       da[r >> 3][r & 7] = (e16)(p[r] * (dpv - d4[e]));
     }
   }

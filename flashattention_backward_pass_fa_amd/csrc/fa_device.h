@@ -226,6 +226,30 @@ __device__ __forceinline__ uint32_t dropout_keep_lane(const MaskArgs& m, int b, 
   return dropout_keep8(m, b, h, i, j0 + 4 * g) | (dropout_keep8(m, b, h, i, j0 + 16 + 4 * g) << 8);
 }
 
+// The same eight keep decisions as dropout_keep8 (position q: half q % 2
+// of word q / 2 against the threshold), laid out for the key-octet trade:
+// position q at bit (q / 2) + 4 (q % 2).  Both halves of a word are tested
+// by two packed 16-bit instructions: a saturating subtraction of
+// threshold - 1 leaves a half nonzero iff it is >= threshold (threshold >= 1
+// whenever dropout is on), and a minimum with 1 turns that into bits 0 and
+// 16.  (Written as instructions: the compiler turns the same expression
+// into two compares and two selects per word.)
+__device__ __forceinline__ uint32_t dropout_keep8_split(const MaskArgs& m, int b, int h, int i, int j0) {
+  const u32x4 x = philox4x32_10(m.off_lo, m.off_hi, ((uint32_t)i << 16) | (uint32_t)j0,
+                                ((uint32_t)b << 16) | (uint32_t)h, m.seed_lo, m.seed_hi);
+  const uint32_t tm1 = (m.keep_threshold - 1u) & 0xFFFFu;
+  const uint32_t t2 = tm1 | (tm1 << 16), ones = 0x00010001u;
+  uint32_t v = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t xw = x[w];
+    uint32_t y;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp\n\tv_pk_min_u16 %0, %0, %3" : "=&v"(y) : "v"(xw), "s"(t2), "s"(ones));
+    v |= y << w;
+  }
+  return (v | (v >> 12)) & 0xFFu;
+}
+
 // Word e of a key octet's trade (dropout_keep_octet): QP broadcasts quad
 // lane e's draws to its quad; a rotation by eight lanes (DPP row_ror:8) of
 // that brings the other quad's lane e.  The quad with key bit 3 clear drew
@@ -242,21 +266,36 @@ __device__ __forceinline__ uint32_t octet_trade(uint32_t mine, int hq) {
 // inside the lane.  The eight lanes of a block (two quads eight lanes
 // apart) share each row's Philox block: the lane with key bit 3 = hq and
 // key % 4 = e draws rows rr = 2 hq and 2 hq + 1, and the eight trade them.
-// Bit 8 rr + (the key's position in its block) of kq[e] is the keep bit of
-// row q0 + 8 rr + 4 g + e.  Every lane of the wave must call it.
+// Bit 8 rr + dropout_octet_bit(key) of kq[e] is the keep bit of row
+// q0 + 8 rr + 4 g + e.  Every lane of the wave must call it.
 __device__ __forceinline__ void dropout_keep_octet(const MaskArgs& m, int b, int h, int q0, int g,
                                                    int key, uint32_t (&kq)[4]) {
   const int hq = (key >> 3) & 1, j0 = (key & ~15) | (key & 4);
   const int row = q0 + 16 * hq + 4 * g + (key & 3);  // rr = 2 hq
-  const uint32_t mine = dropout_keep8(m, b, h, row, j0) | (dropout_keep8(m, b, h, row + 8, j0) << 8);
+  const uint32_t mine = dropout_keep8_split(m, b, h, row, j0) | (dropout_keep8_split(m, b, h, row + 8, j0) << 8);
   kq[0] = octet_trade<0x00>(mine, hq);  // quad_perm [0,0,0,0]
   kq[1] = octet_trade<0x55>(mine, hq);  // quad_perm [1,1,1,1]
   kq[2] = octet_trade<0xAA>(mine, hq);  // quad_perm [2,2,2,2]
   kq[3] = octet_trade<0xFF>(mine, hq);  // quad_perm [3,3,3,3]
 }
 
+// All ones if bit `pos` of `bits` is set, else zero (a signed one-bit field
+// extract), and a float kept or zeroed by such a mask (+0 when zeroed, as a
+// select would give).
+__device__ __forceinline__ uint32_t bit_mask(uint32_t bits, int pos) {
+  return (uint32_t)__builtin_amdgcn_sbfe((int)bits, pos, 1);
+}
+__device__ __forceinline__ float masked(float v, uint32_t m) { return __uint_as_float(__float_as_uint(v) & m); }
+
 // Position of key `key` in its Philox block (bit index in dropout_keep8).
 __device__ __forceinline__ int dropout_pos(int key) { return ((key >> 1) & 4) | (key & 3); }
+
+// Bit of key `key` inside a byte of dropout_keep_octet's words (the
+// position's bit in dropout_keep8_split).
+__device__ __forceinline__ int dropout_octet_bit(int key) {
+  const int q = dropout_pos(key);
+  return (q >> 1) + 4 * (q & 1);
+}
 
 // Address of row `row` (0 <= row < 2^31) of one head whose rows are `rs`
 // bytes apart (rs < 2^32): a single 32 x 32 -> 64-bit multiply-add.

@@ -24,7 +24,7 @@ __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const
                                         const float* sLq, const float* sDq, int g, int b, int h,
                                         int q0, int key, e16x4 (&pw)[4], e16x4 (&dw)[4]) {
   uint32_t kq[4] = {~0u, ~0u, ~0u, ~0u};
-  const int t = dropout_pos(key);
+  const int t = dropout_octet_bit(key);
   if (DROP) dropout_keep_octet(a.m, b, h, q0, g, key, kq);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -38,9 +38,9 @@ __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const
       float dpv = dp[r];
       float pk = p;
       if (DROP) {
-        const bool keep = (kq[e] >> (8 * rr + t)) & 1u;
-        pk = keep ? p : 0.f;  // 1 / (1 - p) is applied to dV at the store
-        dpv = keep ? dpv * a.m.keep_scale : 0.f;
+        const uint32_t km = bit_mask(kq[e], 8 * rr + t);  // all ones iff kept
+        pk = masked(p, km);  // 1 / (1 - p) is applied to dV at the store
+        dpv = masked(dpv * a.m.keep_scale, km);
       }
       pw[rr][e] = (e16)pk;
       dw[rr][e] = (e16)(p * (dpv + nd4[e]));
