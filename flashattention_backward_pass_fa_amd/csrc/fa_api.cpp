@@ -299,7 +299,8 @@ fa_status run_bwd(const fa_params* p, const fa_tensor& q, const fa_tensor& k, co
     c.N = p->seqlen;
     c.d = p->head_dim;
     c.dtype = p->dtype;
-    c.sm_scale = p->sm_scale;
+    // under dropout the KV-outer kernel accumulates dS (1 - p): 1 / (1 - p) here
+    c.sm_scale = p->sm_scale * a.m.keep_scale;
     FA_TRY(launched(fa::launch_dq_convert(c, s)));
   }
   return FA_SUCCESS;

@@ -61,18 +61,20 @@ struct KvCfg {
 
 // Elementwise step of one 32x32 S/dP accumulator pair of the KV-outer kernel:
 // P = exp2(S * c - L2), masked, dropout, dS = P (dP - D).  Writes the 16-bit
-// A operands of dV (P~) and dK (dS) for the two 16-query k-steps.
-template <bool GENERAL, bool DROPOK = true>
-__device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s, const f32x16& dp,
-                                               const float* sLq, const float* sDq, int g, int b,
-                                               int h, int q0, int key, e16x8& pa0, e16x8& pa1,
-                                               e16x8& da0, e16x8& da1) {
+// A operands of dV (P~) and dK (dS) for the two 16-query k-steps.  With
+// dropout (DROPNOW) it writes dS (1 - p) = P~ dP - P D (1 - p) instead:
+// 1 / (1 - p) is applied to dV and dK at the store, and sDq holds D (1 - p).
+template <bool GENERAL, bool DROPNOW>
+__device__ __forceinline__ void kv_elementwise_body(const BwdArgs& a, const f32x16& s, const f32x16& dp,
+                                                    const float* sLq, const float* sDq, int g, int b,
+                                                    int h, int q0, int key, e16x8& pa0, e16x8& pa1,
+                                                    e16x8& da0, e16x8& da1) {
   // Dropout: keys across lanes, so the eight lanes of a Philox block share
   // each row's block (bit 8 rr + t of kq[e]: row 8 rr + 4 g + e; t: the
   // key's bit in a byte of the traded words)
   uint32_t kq[4] = {~0u, ~0u, ~0u, ~0u};
   const int t = dropout_octet_bit(key);
-  if (GENERAL && DROPOK && a.m.dropout) dropout_keep_octet(a.m, b, h, q0, g, key, kq);
+  if (DROPNOW) dropout_keep_octet(a.m, b, h, q0, g, key, kq);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4 l4 = *(const f32x4*)(sLq + 8 * rr + 4 * g);
@@ -81,19 +83,9 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
       float p = fast_exp2(s[r] * a.scale_log2 - l4[e]);
-      float dpv = dp[r];
-      float pdrop = p;
-      if (GENERAL) {
-        const int qi = q0 + 8 * rr + 4 * g + e;
-        p = visible(a.m, qi, key) ? p : 0.f;
-        pdrop = p;
-        if (DROPOK && a.m.dropout) {
-          const uint32_t km = bit_mask(kq[e], 8 * rr + t);  // all ones iff kept
-          pdrop = masked(p, km);  // 1 / (1 - p) is applied to dV at the store
-          dpv = masked(dpv * a.m.keep_scale, km);
-        }
-      }
-      const float ds = p * (dpv - d4[e]);
+      if (GENERAL) p = visible(a.m, q0 + 8 * rr + 4 * g + e, key) ? p : 0.f;
+      const float pdrop = DROPNOW ? masked(p, bit_mask(kq[e], 8 * rr + t)) : p;
+      const float ds = DROPNOW ? fmaf(pdrop, dp[r], -(p * d4[e])) : p * (dp[r] - d4[e]);
       if (r < 8) {
         pa0[r] = (e16)pdrop;
         da0[r] = (e16)ds;
@@ -103,6 +95,17 @@ __device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s
       }
     }
   }
+}
+
+template <bool GENERAL, bool DROPOK = true>
+__device__ __forceinline__ void kv_elementwise(const BwdArgs& a, const f32x16& s, const f32x16& dp,
+                                               const float* sLq, const float* sDq, int g, int b,
+                                               int h, int q0, int key, e16x8& pa0, e16x8& pa1,
+                                               e16x8& da0, e16x8& da1) {
+  if (GENERAL && DROPOK && a.m.dropout)
+    kv_elementwise_body<GENERAL, true>(a, s, dp, sLq, sDq, g, b, h, q0, key, pa0, pa1, da0, da1);
+  else
+    kv_elementwise_body<GENERAL, false>(a, s, dp, sLq, sDq, g, b, h, q0, key, pa0, pa1, da0, da1);
 }
 
 // One fully visible 32-query x 32-key tile of a KV-outer wave, without
@@ -136,8 +139,7 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
   e16x8 b0[DT], b1[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) b0[n] = tr_operand(Os, LD, ulo, ulo + 8, 32 * n, lane);
-  float p[16];
-  uint32_t km[16];  // dropout: all ones for a kept element, zero for a dropped one
+  float p[16], pk[16];  // P and (dropout) P~ = P Z
   e16x8 pa[2], da[2];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -146,8 +148,8 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
       p[r] = fast_exp2(sacc[r] * a.scale_log2 - l4[e]);
-      km[r] = DROP ? bit_mask(kq[e], 8 * rr + kt8) : ~0u;
-      pa[r >> 3][r & 7] = (e16)(DROP ? masked(p[r], km[r]) : p[r]);  // 1 / (1 - p) at the dV store
+      pk[r] = DROP ? masked(p[r], bit_mask(kq[e], 8 * rr + kt8)) : p[r];
+      pa[r >> 3][r & 7] = (e16)pk[r];  // 1 / (1 - p) at the dV store
     }
   }
 #pragma unroll
@@ -164,9 +166,9 @@ __device__ __forceinline__ void kv_full_tile(const BwdArgs& a, const e16* qrow, 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * rr + e;
-      float dpv = dpacc[r];
-      if (DROP) dpv = masked(dpv * a.m.keep_scale, km[r]);
-      da[r >> 3][r & 7] = (e16)(p[r] * (dpv - d4[e]));
+      // dropout: dS (1 - p) = P~ dP - P D (1 - p), with 1 / (1 - p) at the dK
+      // store and D (1 - p) in sDq
+      da[r >> 3][r & 7] = (e16)(DROP ? fmaf(pk[r], dpacc[r], -(p[r] * d4[e])) : p[r] * (dpacc[r] - d4[e]));
     }
   }
 #pragma unroll
@@ -264,7 +266,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
     }
     if (tid < C::BR) {
       sL[buf][tid] = pl * kLog2e;
-      sD[buf][tid] = pd;
+      sD[buf][tid] = pd / a.m.keep_scale;  // D (1 - p): exactly D without dropout
     }
   };
 
@@ -382,7 +384,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_atomic_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int kr = kvw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (kr < NK) {
-        at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dk_acc[n][r] * a.sm_scale);
+        at<e16>(a.dk, b, h, kr)[32 * n + c] = (e16)(dk_acc[n][r] * (a.sm_scale * a.m.keep_scale));
         at<e16>(a.dv, b, h, kr)[32 * n + c] = (e16)(dv_acc[n][r] * a.m.keep_scale);
       }
     }
@@ -464,7 +466,7 @@ __device__ __forceinline__ void dkdv_q2_body(BwdArgs& a, int bh, int blk) {
       store8(smem + (2 + buf) * TILE + row * C::LD + col, po[x]);
     }
     if (tid < C::BR) sL[buf][tid] = pld * kLog2e;
-    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = pld;
+    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = pld / a.m.keep_scale;  // D (1 - p): exactly D without dropout
   };
 
   f32x16 dk_acc[C::DT], dv_acc[C::DT];
@@ -526,7 +528,7 @@ __device__ __forceinline__ void dkdv_q2_body(BwdArgs& a, int bh, int blk) {
       e16x8 pa0, pa1, da0, da1;
       const float* sLq = &sL[buf][32 * qh];
       const float* sDq = &sD[buf][32 * qh];
-      kv_elementwise<true, DROP>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);
+      kv_elementwise_body<true, DROP>(a, sacc, dpacc, sLq, sDq, g, b, h, qs, key, pa0, pa1, da0, da1);  // launched with dropout on iff DROP
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         const int u = 2 * qh + u2;
@@ -607,7 +609,7 @@ __device__ __forceinline__ void dkdv_q2_body(BwdArgs& a, int bh, int blk) {
     }
     __syncthreads();
   };
-  finish(dk_acc, a.dk, a.sm_scale);
+  finish(dk_acc, a.dk, a.sm_scale * a.m.keep_scale);  // dropout: dS (1 - p) was accumulated
   finish(dv_acc, a.dv, a.m.keep_scale);  // 1 / (1 - p): exactly 1 without dropout
 }
 

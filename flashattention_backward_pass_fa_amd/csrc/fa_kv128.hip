@@ -35,15 +35,17 @@ __device__ __forceinline__ void kv_p_ds(const BwdArgs& a, const f32x16& s, const
       const int r = 4 * rr + e;
       float p = fast_exp2(s[r] * a.scale_log2 - l4[e]);
       if (MASK) p = visible(a.m, q0 + 8 * rr + 4 * g + e, key) ? p : 0.f;
-      float dpv = dp[r];
-      float pk = p;
+      const float dpv = dp[r];
       if (DROP) {
-        const uint32_t km = bit_mask(kq[e], 8 * rr + t);  // all ones iff kept
-        pk = masked(p, km);  // 1 / (1 - p) is applied to dV at the store
-        dpv = masked(dpv * a.m.keep_scale, km);
+        // dS (1 - p) = P~ dP - P D (1 - p): 1 / (1 - p) is applied to dV and
+        // dK at the store, and nd4 holds -D (1 - p)
+        const float pk = masked(p, bit_mask(kq[e], 8 * rr + t));
+        pw[rr][e] = (e16)pk;
+        dw[rr][e] = (e16)fmaf(pk, dpv, p * nd4[e]);
+      } else {
+        pw[rr][e] = (e16)p;
+        dw[rr][e] = (e16)(p * (dpv + nd4[e]));
       }
-      pw[rr][e] = (e16)pk;
-      dw[rr][e] = (e16)(p * (dpv + nd4[e]));
     }
   }
 }
@@ -168,7 +170,7 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
   };
   auto ld_store = [&](int buf) {
     if (tid < C::BR) sL[buf][tid] = pld * kLog2e;
-    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = -pld;  // -D: the start value of dP - D
+    else if (tid < 2 * C::BR) sD[buf][tid - C::BR] = -pld / a.m.keep_scale;  // -D (1 - p): the start value of dP - D without dropout
   };
 
   // Query blocks [itA, itB) see all 128 keys with no mask edge: the first
@@ -450,7 +452,7 @@ __device__ __forceinline__ void dkdv_ws_body(BwdArgs& a, int bh, int blk) {
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * m + 8 * (r >> 2) + 4 * g + (r & 3);
         smem[row * SR + n0 + c] = (e16)(acc_v[m][r] * a.m.keep_scale);
-        smem[(C::BC + row) * SR + n0 + c] = (e16)(acc_k[m][r] * a.sm_scale);
+        smem[(C::BC + row) * SR + n0 + c] = (e16)(acc_k[m][r] * (a.sm_scale * a.m.keep_scale));
       }
   }
 
