@@ -720,8 +720,10 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
   for (int n = 0; n < C::DT; ++n) dq_acc[n] = f32x16{};
 
   // dP^T accumulates from -D, so that without dropout the product ends as
-  // dP - D; with dropout from -D (1 - p), so that a kept element's
-  // dP / (1 - p) - D is one multiply (a dropped one is -D)
+  // dP - D; with dropout from -D (1 - p), so that it ends as
+  // (dP / (1 - p) - D) (1 - p) for a kept element, and a dropped one's
+  // -D (1 - p) is the start value itself: the wave forms dS (1 - p), and the
+  // dQ store applies 1 / (1 - p)
   f32x16 dp0;
   {
     const float start = DROP ? -dd / a.m.keep_scale : -dd;
@@ -801,7 +803,7 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
           float p = fast_exp2(st[r] * a.scale_log2 - l2);
           float dmd = dpt[r];  // dP - D (dropout: with dP scaled by 1 - p)
           p = visible(a.m, myq, j4 + e) ? p : 0.f;
-          if (DROP) dmd = (keep >> e) & 1u ? dmd * a.m.keep_scale : -dd;
+          if (DROP) dmd = (keep >> e) & 1u ? dmd : dp0[0];  // dS (1 - p): 1 / (1 - p) at the dQ store
           const e16 v = (e16)(p * dmd);
           if (r < 8) d0[r] = v; else d1[r - 8] = v;
         }
@@ -825,7 +827,7 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
           float dmd = dpt[r];
-          if (FDROP) dmd = (keep >> e) & 1u ? dmd * a.m.keep_scale : -dd;
+          if (FDROP) dmd = (keep >> e) & 1u ? dmd : dp0[0];  // dS (1 - p): 1 / (1 - p) at the dQ store
           const e16 v = (e16)(fast_exp2(st[r] * a.scale_log2 - l2) * dmd);
           if (r < 8) d0[r] = v; else d1[r - 8] = v;
         }
@@ -884,7 +886,7 @@ __device__ __forceinline__ void dq_body(BwdArgs& a, int bh, int blk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           stage[(32 * lw + 8 * (r >> 2) + 4 * g + (r & 3)) * SR + 32 * n + c] =
-              (e16)(dq_acc[n][r] * a.sm_scale);
+              (e16)(dq_acc[n][r] * (DROP ? a.sm_scale * a.m.keep_scale : a.sm_scale));
     }
     __syncthreads();
 #pragma unroll
